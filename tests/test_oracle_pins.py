@@ -1,0 +1,427 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+* exact decimal brute force (50 significant digits) on tiny inputs;
+* closed forms (one and two positions, zero query, tied keys, a spike key);
+* independent library routines (scipy's logsumexp / softmax, torch's E4M3FN);
+* invariants the pages fix (Kimi K3 on MI355X, section 4 "MLA": heads are
+  independent, so padding heads changes no real head, and splitting the history
+  into partitions then combining changes nothing; section 1 "Cache", DCP8
+  paragraph: shard partials merged with their normalisation equal the unsharded
+  answer, and 8x heads over 1/8 of the history keeps the arithmetic unchanged);
+* the pages' own worked numbers (the DCP8 payload estimate, tests/golden).
+
+Each pin is a function taking the oracle routine(s) it checks, so that the
+mutation tests at the end can plant a mistake in a copy of the oracle and show
+that some pin fails.
+"""
+
+import decimal
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from mla_split_kv_decode_amd import workloads as wk
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TAU = float(np.float32(1.0 / math.sqrt(192.0)))
+
+
+def bf16_values(rng, shape, scale=1.0):
+    """Random values exactly representable in bf16 (via the generator's cast)."""
+    bits = wk.to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * scale)
+    return oracle.bf16_bits_to_f64(bits)
+
+
+# ------------------------------------------------------------------ P1 decimal
+
+def decimal_attention(q_rows, x, tau, prec=50):
+    """Softmax attention in exact decimal arithmetic (prec significant digits)."""
+    ctx = decimal.Context(prec=prec)
+    D = decimal.Decimal
+    tau_d = D(tau)
+    xs = [[D(float(v)) for v in row] for row in x]
+    outs, lses = [], []
+    for q in q_rows:
+        qd = [D(float(v)) for v in q]
+        s = [ctx.multiply(tau_d, sum((a * b for a, b in zip(qd, row)), D(0))) for row in xs]
+        m = max(s)
+        w = [ctx.exp(si - m) for si in s]
+        l = sum(w, D(0))
+        o = []
+        for e in range(oracle.D_V):
+            acc = sum((wj * row[e] for wj, row in zip(w, xs)), D(0))
+            o.append(float(ctx.divide(acc, l)))
+        outs.append(o)
+        lses.append(float(m + ctx.ln(l)))
+    return np.array(outs), np.array(lses)
+
+
+def pin_decimal(attention_fn, cases=((1, 1), (2, 2), (3, 3), (1, 5), (2, 8))):
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for n_rows, n in cases:
+        q = bf16_values(rng, (n_rows, oracle.D_LATENT))
+        x = bf16_values(rng, (n, oracle.D_LATENT))
+        o, lse = attention_fn(q, x, TAU)
+        od, lsed = decimal_attention(q, x, TAU)
+        worst = max(worst, float(np.abs(o - od).max()), float(np.abs(lse - lsed).max()))
+    return worst
+
+
+def test_decimal_brute_force():
+    assert pin_decimal(oracle.attention) <= 1e-12
+
+
+def decimal_decode_paged(wl, r, t, h):
+    """One output row of a paged workload, with the causal reading written out
+    independently of the oracle (token t of T sees the first L - T + t + 1
+    positions) and every position gathered one by one."""
+    L = int(wl.seq_lens[r])
+    n = L - wl.q_len + t + 1
+    rows = []
+    for j in range(n):
+        page = int(wl.block_table[r][j // wl.page_size])
+        rows.append(oracle.bf16_bits_to_f64(wl.pool[page, j % wl.page_size]))
+    q = oracle.bf16_bits_to_f64(wl.q_bits[r, t, h])[None]
+    return decimal_attention(q, np.array(rows), float(wl.softmax_scale), prec=40)
+
+
+def test_decimal_paged_decode():
+    wl = wk.make_workload(None, seed=5, batch=2, q_len=2, num_heads=3, seq_lens=[70, 5],
+                          kv_format="bf16", shuffled=True)
+    o, lse = oracle.decode_paged(wl.q_bits, wl.pool, "bf16", 1.0, wl.block_table, wl.seq_lens,
+                                 wl.page_size, wl.softmax_scale, causal=True)
+    for r, t, h in [(0, 0, 0), (0, 1, 2), (1, 0, 1), (1, 1, 0)]:
+        od, lsed = decimal_decode_paged(wl, r, t, h)
+        assert np.abs(o[r, t, h] - od[0]).max() <= 1e-12
+        assert abs(lse[r, t, h] - lsed[0]) <= 1e-12
+
+
+# ------------------------------------------------------------- P2 closed forms
+
+def pin_closed_forms(attention_fn):
+    """Return a list of (name, error) for the closed-form cases."""
+    rng = np.random.default_rng(12)
+    out = []
+    q = bf16_values(rng, (2, oracle.D_LATENT))
+    x = bf16_values(rng, (2, oracle.D_LATENT))
+    # one position: O is that position's value row, LSE its score
+    o, lse = attention_fn(q, x[:1], TAU)
+    s0 = TAU * np.array([math.fsum(q[i] * x[0]) for i in range(2)])
+    out.append(("n1_value", float(np.abs(o - x[0, :oracle.D_V][None]).max())))
+    out.append(("n1_lse", float(np.abs(lse - s0).max())))
+    # two positions: logistic weights, LSE = logaddexp
+    o, lse = attention_fn(q, x, TAU)
+    s = TAU * np.array([[math.fsum(q[i] * x[j]) for j in range(2)] for i in range(2)])
+    w0 = 1.0 / (1.0 + np.exp(s[:, 1] - s[:, 0]))
+    ref = w0[:, None] * x[0, :oracle.D_V] + (1 - w0)[:, None] * x[1, :oracle.D_V]
+    out.append(("n2_value", float(np.abs(o - ref).max())))
+    out.append(("n2_lse", float(np.abs(lse - np.logaddexp(s[:, 0], s[:, 1])).max())))
+    # zero query (a zero-padded head): O = mean of V, LSE = ln n
+    xn = bf16_values(rng, (37, oracle.D_LATENT))
+    o, lse = attention_fn(np.zeros((1, oracle.D_LATENT)), xn, TAU)
+    out.append(("zero_q_value", float(np.abs(o[0] - xn[:, :oracle.D_V].mean(axis=0)).max())))
+    out.append(("zero_q_lse", abs(float(lse[0]) - math.log(37))))
+    # query only on the 64 trailing (rotary) columns, keys tied there: every
+    # score equals s, so O = mean of the first 512 columns and LSE = s + ln n.
+    qr = np.zeros((1, oracle.D_LATENT))
+    qr[0, oracle.D_V:] = bf16_values(rng, (64,))
+    xt = bf16_values(rng, (9, oracle.D_LATENT))
+    xt[:, oracle.D_V:] = xt[0, oracle.D_V:]
+    o, lse = attention_fn(qr, xt, TAU)
+    st = TAU * math.fsum(qr[0, oracle.D_V:] * xt[0, oracle.D_V:])
+    out.append(("tied_value", float(np.abs(o[0] - xt[:, :oracle.D_V].mean(axis=0)).max())))
+    out.append(("tied_lse", abs(float(lse[0]) - (st + math.log(9)))))
+    # spike: one key along q with a huge score takes all the weight
+    xs = bf16_values(rng, (16, oracle.D_LATENT))
+    qs = bf16_values(rng, (1, oracle.D_LATENT))
+    xs[5] = 64.0 * np.sign(qs[0])
+    o, _ = attention_fn(qs, xs, TAU)
+    out.append(("spike_value", float(np.abs(o[0] - xs[5, :oracle.D_V]).max())))
+    return out
+
+
+def test_closed_forms():
+    errs = dict(pin_closed_forms(oracle.attention))
+    assert errs["n1_value"] == 0.0
+    for name, err in errs.items():
+        assert err <= 1e-12, (name, err)
+
+
+def pin_library(attention_fn):
+    """scipy's logsumexp and softmax on independently computed scores."""
+    from scipy.special import logsumexp, softmax
+
+    rng = np.random.default_rng(13)
+    q = bf16_values(rng, (5, oracle.D_LATENT))
+    x = bf16_values(rng, (300, oracle.D_LATENT))
+    s = TAU * np.einsum("rd,nd->rn", q, x)
+    o, lse = attention_fn(q, x, TAU)
+    e_lse = float(np.abs(lse - logsumexp(s, axis=1)).max())
+    e_o = float(np.abs(o - softmax(s, axis=1) @ x[:, :oracle.D_V]).max())
+    return max(e_lse, e_o)
+
+
+def test_library_routines():
+    assert pin_library(oracle.attention) <= 1e-12
+
+
+# --------------------------------------------------------------- P3 invariants
+
+def pin_split_merge(attention_fn, merge_fn, seed=14):
+    """Random covers of the history (empty pieces included, any order):
+    merging the pieces' (O, LSE) equals attending over the whole history."""
+    rng = np.random.default_rng(seed)
+    q = bf16_values(rng, (4, oracle.D_LATENT))
+    x = bf16_values(rng, (1000, oracle.D_LATENT))
+    o_ref, lse_ref = attention_fn(q, x, TAU)
+    worst = 0.0
+    for parts in (1, 2, 4, 16, 33):
+        cuts = np.sort(rng.integers(0, 1001, size=parts - 1))
+        bounds = np.concatenate([[0], cuts, [1000]])
+        pieces = [attention_fn(q, x[a:b], TAU) for a, b in zip(bounds[:-1], bounds[1:])]
+        order = rng.permutation(len(pieces))
+        o, lse = merge_fn(np.stack([pieces[i][0] for i in order]),
+                          np.stack([pieces[i][1] for i in order]))
+        worst = max(worst, float(np.abs(o - o_ref).max()), float(np.abs(lse - lse_ref).max()))
+    return worst
+
+
+def test_split_merge_equals_unsplit():
+    assert pin_split_merge(oracle.attention, oracle.merge) <= 1e-13
+
+
+def test_merge_all_empty():
+    o, lse = oracle.merge(np.zeros((3, 2, oracle.D_V)), np.full((3, 2), -np.inf))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    # one live part among empties passes through unchanged
+    o_live = np.arange(2 * oracle.D_V, dtype=np.float64).reshape(2, oracle.D_V)
+    lse_parts = np.array([[-np.inf, -np.inf], [1.5, -2.0], [-np.inf, -np.inf]])
+    o_parts = np.zeros((3, 2, oracle.D_V))
+    o_parts[1] = o_live
+    o, lse = oracle.merge(o_parts, lse_parts)
+    assert np.array_equal(o, o_live) and np.array_equal(lse, [1.5, -2.0])
+
+
+def test_head_padding_leaves_real_heads():
+    """12 real heads padded to 16 with zero rows or with copies of real heads."""
+    rng = np.random.default_rng(15)
+    q = bf16_values(rng, (1, 1, 12, oracle.D_LATENT))
+    x = [bf16_values(rng, (777, oracle.D_LATENT))]
+    o12, l12 = oracle.decode(q, x, TAU)
+    for pad in ("zero", "copy"):
+        q16 = np.zeros((1, 1, 16, oracle.D_LATENT))
+        q16[:, :, :12] = q
+        if pad == "copy":
+            q16[:, :, 12:] = q[:, :, :4]
+        o16, l16 = oracle.decode(q16, x, TAU)
+        assert np.abs(o16[:, :, :12] - o12).max() <= 1e-15
+        assert np.abs(l16[:, :, :12] - l12).max() <= 1e-15
+        if pad == "zero":  # a zero pad head weighs every position alike
+            assert np.abs(l16[0, 0, 12:] - math.log(777)).max() <= 1e-12
+            assert np.abs(o16[0, 0, 12:] - x[0][:, :oracle.D_V].mean(axis=0)).max() <= 1e-12
+
+
+def test_page_permutation_invariance():
+    """The same logical history under two different physical page layouts."""
+    wl = wk.make_workload(None, seed=16, batch=3, q_len=1, num_heads=4,
+                          seq_lens=[200, 64, 129], shuffled=True)
+    rng = np.random.default_rng(17)
+    perm = rng.permutation(wl.num_pages)
+    pool2 = np.empty_like(wl.pool)
+    pool2[perm] = wl.pool  # physical page p moves to perm[p]
+    table2 = np.where(wl.block_table >= 0, perm[np.maximum(wl.block_table, 0)], -1)
+    a = oracle.decode_paged(wl.q_bits, wl.pool, "bf16", 1.0, wl.block_table, wl.seq_lens,
+                            64, wl.softmax_scale)
+    b = oracle.decode_paged(wl.q_bits, pool2, "bf16", 1.0, table2, wl.seq_lens, 64,
+                            wl.softmax_scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def pin_causal_drafts(decode_fn):
+    """Causal masking among T drafts (the last T cached positions).
+
+    Returns a list of failures.  Token t must not depend on the latents of
+    later drafts, must depend on its own latent, and must equal a one-token
+    decode over the first L - T + t + 1 positions.
+    """
+    rng = np.random.default_rng(18)
+    T, L, H = 4, 70, 3
+    q = bf16_values(rng, (1, T, H, oracle.D_LATENT))
+    x = bf16_values(rng, (L, oracle.D_LATENT))
+    o, lse = decode_fn(q, [x], TAU)
+    bad = []
+    for t in range(T):
+        o1, lse1 = decode_fn(q[:, t:t + 1], [x[:L - T + t + 1]], TAU)
+        if not (np.abs(o1[0, 0] - o[0, t]).max() <= 1e-14 and
+                np.abs(lse1[0, 0] - lse[0, t]).max() <= 1e-14):
+            bad.append(("single_token", t))
+    # spike the latent of draft d (position L - T + d) towards every query
+    for d in range(T):
+        xs = x.copy()
+        xs[L - T + d] = 40.0 * np.sign(q[0, 0, 0])
+        os_, _ = decode_fn(q, [xs], TAU)
+        for t in range(T):
+            changed = np.abs(os_[0, t] - o[0, t]).max() > 1e-6
+            if changed != (d <= t):
+                bad.append(("spike", d, t))
+    return bad
+
+
+def test_causal_among_drafts():
+    assert pin_causal_drafts(oracle.decode) == []
+
+
+def pin_dcp(decode_fn, merge_fn, layout):
+    """DCP8 emulation: each shard decodes its local positions; merging the
+    shards' (O, LSE) equals the unsharded decode."""
+    rng = np.random.default_rng(19)
+    B, H, L, ways = 2, 6, 8 * 150, 8
+    q = bf16_values(rng, (B, 1, H, oracle.D_LATENT))
+    xs = [bf16_values(rng, (L, oracle.D_LATENT)) for _ in range(B)]
+    o_ref, lse_ref = decode_fn(q, xs, TAU)
+    pos = np.arange(L)
+    if layout == "contiguous":
+        owner = pos // (L // ways)
+    else:  # round-robin by 64-position page
+        owner = (pos // 64) % ways
+    parts = [decode_fn(q, [x[owner == s] for x in xs], TAU) for s in range(ways)]
+    o, lse = merge_fn(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    return max(float(np.abs(o - o_ref).max()), float(np.abs(lse - lse_ref).max()))
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "round_robin_pages"])
+def test_dcp_shard_merge(layout):
+    assert pin_dcp(oracle.decode, oracle.merge, layout) <= 1e-13
+
+
+# --------------------------------------------------------- P4 / P6 counters
+
+def test_work_conservation_dcp8():
+    """8x the heads over 1/8 of the history: the same attention arithmetic."""
+    g = json.load(open(os.path.join(GOLDEN, "payload_k3.json")))
+    n = g["positions"]
+    heads_tp = g["tp_heads_total"] // g["tp_ways"]
+    assert heads_tp == g["printed_heads_per_gpu_tp8"]
+    a = wk.attention_flops([n // g["dcp_ways"]], 1, g["tp_heads_total"])
+    b = wk.attention_flops([n], 1, heads_tp)
+    assert a == b
+
+
+def test_payload_bytes_match_page():
+    g = json.load(open(os.path.join(GOLDEN, "payload_k3.json")))
+    per_layer = wk.kv_bytes([g["positions"]], "fp8_e4m3fn")
+    total = g["mla_layers"] * per_layer
+    assert total == 1_963_008_000
+    assert round(total / 1e9, 2) == g["printed_payload_gb_per_gpu"]
+    assert round(total / g["dcp_ways"] / 1e6) == g["printed_dcp8_payload_mb_per_gpu"]
+
+
+# -------------------------------------------------------------- P5 FP8 codec
+
+def test_e4m3fn_codec_all_codes():
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3fn_codes_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(mine) & np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.all(both_nan | (mine == ref))
+    assert set(np.flatnonzero(np.isnan(mine))) == {0x7F, 0xFF}
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+
+
+def test_e4m3fn_quantiser():
+    vals = np.array([1.0625, 1.1875, 448.0, -448.0, 2.0 ** -10, 3 * 2.0 ** -11, 0.0],
+                    dtype=np.float32)
+    codes = wk.to_e4m3fn_codes(vals)
+    dec = oracle.e4m3fn_codes_to_f64(codes)
+    # ties to even: 1.0625 -> 1.0, 1.1875 -> 1.25; 2^-10 ties to 0, 3*2^-11 -> 2^-9
+    assert list(dec) == [1.0, 1.25, 448.0, -448.0, 0.0, 2.0 ** -9, 0.0]
+    wl = wk.make_workload(None, seed=20, batch=2, q_len=1, num_heads=2, seq_lens=[100, 30],
+                          kv_format="fp8_e4m3fn")
+    valid = np.concatenate([oracle.gather_latents(wl.pool, wl.block_table[r], int(L), 64)
+                            for r, L in enumerate(wl.seq_lens)])
+    assert not np.any((valid & 0x7F) == 0x7F)  # no NaN in valid data
+    assert np.max(np.abs(oracle.e4m3fn_codes_to_f64(valid))) == 448.0
+
+
+def test_generator_pins():
+    wl = wk.make_workload("ragged")
+    assert list(wl.seq_lens[:5]) == [26785, 3742, 6720, 8541, 6781]
+    assert int(wl.seq_lens.sum()) == 1_002_597
+    assert wl.num_pages - wk.SPARE_PAGES == 15_698
+    assert wk.kv_bytes(wl.seq_lens, "bf16") == 1_154_991_744
+
+
+def test_generator_poison():
+    wl = wk.make_workload(None, seed=21, batch=2, q_len=1, num_heads=2, seq_lens=[65, 3])
+    # the tail slots of each request's last page and the spare pages are NaN
+    assert np.all(wl.pool[wl.block_table[0, 1], 1:] == wk.BF16_NAN)
+    assert np.all(wl.pool[wl.block_table[1, 0], 3:] == wk.BF16_NAN)
+    assert np.all(wl.pool[wl.extra["spare_pages"]] == wk.BF16_NAN)
+    assert not np.any(np.isnan(oracle.decode_paged(
+        wl.q_bits, wl.pool, "bf16", 1.0, wl.block_table, wl.seq_lens, 64,
+        wl.softmax_scale)[0]))
+
+
+# --------------------------------------------- mutations planted in the oracle
+
+def _attention_mutant(kind):
+    def fn(q_rows, x, softmax_scale):
+        q_rows = np.asarray(q_rows, dtype=np.float64)
+        x = np.asarray(x, dtype=np.float64)
+        tau = float(softmax_scale)
+        if x.shape[0] == 0:
+            return np.zeros((q_rows.shape[0], oracle.D_V)), np.full(q_rows.shape[0], -np.inf)
+        if kind == "k_512_only":
+            s = tau * (x[:, :oracle.D_V] @ q_rows[:, :oracle.D_V].T)
+        elif kind == "no_scale":
+            s = x @ q_rows.T
+        else:
+            s = tau * (x @ q_rows.T)
+        m = s.max(axis=0)
+        w = np.exp(s - m)
+        l = w.sum(axis=0)
+        v = x[:, 64:] if kind == "v_last_512" else x[:, :oracle.D_V]
+        o = (w.T @ v) / l[:, None]
+        lse = m + np.log(l) if kind != "lse_log2" else m + np.log2(l)
+        return o, lse
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["k_512_only", "no_scale", "v_last_512", "lse_log2"])
+def test_mutants_fail_a_pin(kind):
+    fn = _attention_mutant(kind)
+    errs = [pin_decimal(fn, cases=((2, 3),)), max(e for _, e in pin_closed_forms(fn))]
+    assert max(errs) > 1e-6
+
+
+def test_merge_mutant_fails():
+    def plain_average(o_parts, lse_parts):
+        return np.mean(o_parts, axis=0), np.max(lse_parts, axis=0)
+    assert pin_split_merge(oracle.attention, plain_average) > 1e-3
+
+
+def test_causal_mutants_fail():
+    def shifted(delta):
+        def decode_fn(q, latents, softmax_scale):
+            T = q.shape[1]
+            outs = []
+            for r, x in enumerate(latents):
+                L = x.shape[0]
+                rows = [oracle.attention(q[r, t], x[:max(0, min(L, L - T + t + 1 + delta))],
+                                         softmax_scale) for t in range(T)]
+                outs.append(rows)
+            o = np.array([[row[0] for row in req] for req in outs])
+            lse = np.array([[row[1] for row in req] for req in outs])
+            return o, lse
+        return decode_fn
+    assert pin_causal_drafts(shifted(0)) == []
+    assert pin_causal_drafts(shifted(-1)) != []
+    assert pin_causal_drafts(shifted(+1)) != []
