@@ -1,0 +1,57 @@
+"""Build ``libmla_decode.so`` in-tree with hipcc for gfx950.
+
+    python -m mla_split_kv_decode_amd.build [-v]
+
+The library holds the HIP kernels and the C ABI of ``include/mla_decode.h``.
+"""
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+REPO = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libmla_decode.so")
+SOURCES = ["mla_kernels.hip", "mla_api.hip"]
+ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def command(out=LIB, extra=()):
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed-fp32 VALU forms are kept out of the device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        "-I", os.path.join(REPO, "include"), "-I", CSRC,
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        *extra, "-o", out,
+    ]
+
+
+def build(verbose=False):
+    """Compile the library (always, even when one is already built)."""
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

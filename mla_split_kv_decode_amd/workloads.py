@@ -226,3 +226,28 @@ def io_bytes(seq_lens, q_len, num_heads, kv_format, with_lse=True):
     rows = b * q_len * num_heads
     return (kv_bytes(seq_lens, kv_format) + rows * D_LATENT * 2 + rows * D_V * 2
             + (rows * 4 if with_lse else 0) + pages * 4 + b * 4)
+
+
+# ------------------------------------------------------------- device staging
+
+def to_device(wl, device="cuda", pool=None):
+    """Copy a workload's inputs to device tensors (plumbing only).
+
+    Returns a dict: q (bf16 [B][T][H][576]), pool (bf16 or uint8
+    [num_pages][64][576]), block_table and seq_lens (int32), kv_scale (float).
+    """
+    import torch
+
+    pool = wl.pool if pool is None else pool
+    q = torch.from_numpy(wl.q_bits.view(np.int16)).to(device).view(torch.bfloat16)
+    if wl.kv_format == "bf16":
+        pool_t = torch.from_numpy(pool.view(np.int16)).to(device).view(torch.bfloat16)
+    else:
+        pool_t = torch.from_numpy(pool).to(device)
+    return {
+        "q": q,
+        "pool": pool_t,
+        "block_table": torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(device),
+        "seq_lens": torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).to(device),
+        "kv_scale": float(wl.kv_scale),
+    }
