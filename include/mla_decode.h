@@ -105,7 +105,7 @@ typedef struct {
  *   q_len         query tokens per request, T >= 1 (T > 1: multi-token verification)
  *   num_heads     real query heads H >= 1; rows are padded to a multiple of 16 inside
  *                 the kernel (padding rows are never loaded or written).  Limit:
- *                 q_len * ceil(H/16) <= 16.
+ *                 q_len * ceil(H/16) <= 8.
  *   softmax_scale scale applied to q.k (e.g. 1/sqrt(192)), finite and > 0
  *   causal        1: token t sees positions 0 .. L-T+t; 0: every token sees all L
  *   num_splits    history partitions per request: 0 = automatic (pages balanced over
@@ -157,22 +157,41 @@ int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity);
  *   q          bf16 [batch][q_len][num_heads][576], 16-byte aligned
  *   kv         paged latent KV (kv->kv_dtype must match the plan's)
  *   workspace  device scratch of at least the plan's workspace_bytes, 256-byte
- *              aligned.  Holds the partial answers between the two stages; its
- *              contents need no initialisation and are overwritten.
+ *              aligned.  Bytes [0, 256) are control words of the single-launch path
+ *              (see mla_workspace_init); the rest holds the partial answers between the
+ *              two stages and needs no initialisation.
  *   out        [batch][q_len][num_heads][512] of out_dtype (MLA_BF16, rounded to
  *              nearest even, or MLA_FP32), 16-byte aligned, or NULL
  *   out_lse    fp32 [batch][q_len][num_heads] natural-log LSE, or NULL.  With it the
  *              result is a DCP shard's partial answer (section 1): merge shards with
  *              mla_merge_lse.
  * With out == NULL and out_lse == NULL only the partial stage runs; the partials stay
- * in the workspace: fp32 O [num_parts][q_len*num_heads][512] at byte 0, then fp32 LSE
+ * in the workspace: fp32 O [num_parts][q_len*num_heads][512] at byte 256, then fp32 LSE
  * [num_parts][q_len*num_heads] at the next 256-byte boundary (rows ordered token-major,
  * then head).
+ * When all of the plan's workgroups fit on the device at once, both stages run in one
+ * kernel whose workgroups meet at a device-wide barrier kept in the workspace's control
+ * words; otherwise (or with the environment variable MLA_SINGLE_LAUNCH=0) two kernels
+ * run back to back.  Results are identical either way.  In the single-launch path, a
+ * workspace whose control words were not initialised (mla_workspace_init) yields NaN
+ * outputs, never a hang; a barrier wait that exceeds its bound (about 0.1 s) also
+ * yields NaN and marks the control words, so later calls yield NaN until the workspace
+ * is initialised again.
  * Calls that share a workspace must be ordered on one stream.
  */
 mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_paged_kv* kv,
                               void* workspace, size_t workspace_bytes, void* out,
                               int32_t out_dtype, float* out_lse, void* stream);
+
+/*
+ * Initialise the control words (bytes [0, 256)) of a workspace for the single-launch
+ * path: once per workspace, before its first mla_decode_splitkv, whatever plans later use
+ * it; every completed call leaves them ready for the next.  Enqueued on `stream` as a
+ * small kernel (safe to capture in a graph).  For callers that allocate a workspace and
+ * keep it; no allocation happens here.
+ */
+mla_status mla_workspace_init(const mla_plan* plan, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Merge partial answers that carry their LSE (section 1, DCP8 paragraph; section 4,

@@ -68,6 +68,7 @@ def _signatures():
         "mla_decode_splitkv": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_size_t, P, c.c_int32,
                                          P, P]),
         "mla_merge_lse": (c.c_int, [P, c.c_int32, P, c.c_int32, c.c_int64, P, c.c_int32, P, P]),
+        "mla_workspace_init": (c.c_int, [P, P, c.c_size_t, P]),
         "mla_block_table_check": (c.c_int, [P, c.c_int32, c.c_int32, P, c.c_int32, c.c_int64]),
         "mla_page_bytes": (c.c_size_t, [c.c_int32, c.c_int32]),
         "mla_status_str": (c.c_char_p, [c.c_int]),
@@ -189,10 +190,18 @@ def paged_kv(pool, block_table, seq_lens, kv_dtype, kv_scale=1.0, page_size=PAGE
                       _ptr(seq_lens))
 
 
-def workspace(plan, device="cuda"):
+def workspace(plan, device="cuda", stream=None):
+    """A device workspace for `plan`, its control words initialised."""
     import torch
 
-    return torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=device)
+    workspace_init(plan, ws, stream)
+    return ws
+
+
+def workspace_init(plan, ws, stream=None):
+    _check(load().mla_workspace_init(plan.handle, _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
 
 
 def decode_splitkv(plan, q, kv, ws, out=None, out_dtype=MLA_BF16, out_lse=None, stream=None):

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -16,6 +17,9 @@
 namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int64_t total_rows, hipStream_t stream);
+hipError_t launch_fused(const PartialParams& p, const MergeParams& mp, uint32_t* ctrl, bool fp8,
+                        hipStream_t stream, bool* launched);
+hipError_t launch_init_ctrl(uint32_t* w, hipStream_t stream);
 int partial_waves_per_row_block(int row_blocks);
 size_t partial_lds_size(bool fp8, int row_blocks);
 }  // namespace mla
@@ -35,7 +39,7 @@ struct mla_plan {
   int32_t num_splits;    // S (SPLIT_FIXED)
   int32_t num_slots;     // partial answers the workspace holds
   int64_t total_pages;
-  size_t o_bytes, lse_offset, workspace_bytes;
+  size_t ctrl_offset, o_offset, o_bytes, lse_offset, workspace_bytes;
   std::vector<int32_t> seq_lens;  // host copy, for get_work only
 };
 
@@ -70,11 +74,18 @@ int wg_per_cu(bool fp8, int row_blocks) {
   return n < 1 ? 1 : (n > 2 ? 2 : n);
 }
 
+// The single-launch path can be switched off with MLA_SINGLE_LAUNCH=0 (then the two
+// kernels run back to back), e.g. to compare the two; read on every call.
+bool fused_enabled() {
+  const char* v = getenv("MLA_SINGLE_LAUNCH");
+  return !(v && v[0] == '0');
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.1.0 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.2.0 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -184,9 +195,13 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   }
   pl->num_wg = (int32_t)wg;
   pl->num_slots = (int32_t)slots;
+  // [control words | fp32 partial O | fp32 partial LSE]; the control words sit at byte 0
+  // for every plan, so one initialisation serves a workspace whatever plan uses it.
+  pl->ctrl_offset = 0;
+  pl->o_offset = kCtrlBytes;
   pl->o_bytes = align256((size_t)slots * pl->rows * kDV * sizeof(float));
-  pl->lse_offset = pl->o_bytes;
-  pl->workspace_bytes = pl->o_bytes + align256((size_t)slots * pl->rows * sizeof(float));
+  pl->lse_offset = pl->o_offset + pl->o_bytes;
+  pl->workspace_bytes = pl->lse_offset + align256((size_t)slots * pl->rows * sizeof(float));
   if (workspace_bytes) *workspace_bytes = pl->workspace_bytes;
   *plan_out = pl;
   return ok();
@@ -269,7 +284,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
 
   const mla_decode_shape& s = plan->shape;
   hipStream_t st = (hipStream_t)stream;
-  float* part_o = (float*)workspace;
+  float* part_o = (float*)((char*)workspace + plan->o_offset);
   float* part_lse = (float*)((char*)workspace + plan->lse_offset);
 
   PartialParams pp{};
@@ -290,14 +305,17 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   pp.mode = plan->mode;
   pp.num_wg = plan->num_wg;
   pp.num_splits = plan->num_splits;
+  pp.total_pages = plan->total_pages;
   const float log2e = 1.44269504088896341f;
   pp.score_scale = s.softmax_scale * log2e * (fp8 ? kv->kv_scale : 1.0f);
   pp.v_scale = fp8 ? kv->kv_scale : 1.0f;
-  if (plan->num_wg > 0) {
-    hipError_t e = launch_partial(pp, fp8, st);
-    if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
+  if (!out && !out_lse) {
+    if (plan->num_wg > 0) {
+      hipError_t e = launch_partial(pp, fp8, st);
+      if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
+    }
+    return ok();
   }
-  if (!out && !out_lse) return ok();
 
   MergeParams mp{};
   mp.part_o = part_o;
@@ -315,8 +333,33 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   mp.split_mode = plan->mode;
   mp.num_wg = plan->num_wg;
   mp.num_splits = plan->num_splits;
-  hipError_t e = launch_merge(mp, (int64_t)s.batch * plan->rows, st);
+  mp.total_pages = plan->total_pages;
+  hipError_t e = hipSuccess;
+  if (plan->num_wg > 0 && fused_enabled()) {
+    bool launched = false;
+    uint32_t* ctrl = (uint32_t*)((char*)workspace + plan->ctrl_offset);
+    e = launch_fused(pp, mp, ctrl, fp8, st, &launched);
+    if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "fused launch: %s", hipGetErrorString(e));
+    if (launched) return ok();
+  }
+  if (plan->num_wg > 0) {
+    e = launch_partial(pp, fp8, st);
+    if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
+  }
+  e = launch_merge(mp, (int64_t)s.batch * plan->rows, st);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mla_status mla_workspace_init(const mla_plan* plan, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!plan || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan->workspace_bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes,
+                plan->workspace_bytes);
+  hipError_t e = launch_init_ctrl((uint32_t*)((char*)workspace + plan->ctrl_offset), (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "init launch: %s", hipGetErrorString(e));
   return ok();
 }
 

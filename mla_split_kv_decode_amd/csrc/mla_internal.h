@@ -41,17 +41,34 @@ constexpr int kMaxRowBlocks = 8;   // q_len * ceil(heads / 16) limit of one work
 
 enum SplitMode : int32_t { SPLIT_BALANCED = 0, SPLIT_FIXED = 1 };
 
+// Control words at the end of the workspace (fused launch): [0] barrier arrivals,
+// [1] barrier generation, [2] marker that the words were initialised.
+constexpr int kCtrlWords = 4;
+constexpr int kCtrlMagicWord = 2;
+constexpr uint32_t kCtrlMagic = 0x4D4C4131u;
+constexpr size_t kCtrlBytes = 256;
+
 // Pages request r reads, from its length and the block-table row length.
 MLA_HD int32_t pages_of(int32_t seq_len, int32_t max_pages) {
   int32_t p = seq_len > 0 ? (seq_len + kPage - 1) / kPage : 0;
   return p < max_pages ? p : max_pages;
 }
 
+// floor(x / y) for 0 <= x < 2^52, 0 < y: a double-precision estimate corrected to the
+// exact quotient with integer multiplies (a 64-bit integer division is a long software
+// sequence on the GPU).
+MLA_HD int64_t div_floor(int64_t x, int64_t y) {
+  int64_t q = (int64_t)((double)x / (double)y);
+  if (q * y > x) --q;
+  if ((q + 1) * y <= x) ++q;
+  return q;
+}
+
 // First global page of workgroup w under SPLIT_BALANCED.
-MLA_HD int64_t balanced_start(int64_t w, int64_t P, int64_t W) { return (w * P) / W; }
+MLA_HD int64_t balanced_start(int64_t w, int64_t P, int64_t W) { return div_floor(w * P, W); }
 
 // Workgroup holding global page g under SPLIT_BALANCED (largest w with start(w) <= g).
-MLA_HD int64_t balanced_wg_of(int64_t g, int64_t P, int64_t W) { return ((g + 1) * W - 1) / P; }
+MLA_HD int64_t balanced_wg_of(int64_t g, int64_t P, int64_t W) { return div_floor((g + 1) * W - 1, P); }
 
 MLA_HD int32_t fixed_page_begin(int32_t s, int32_t pages, int32_t S) {
   return (int32_t)(((int64_t)s * pages) / S);
@@ -72,6 +89,7 @@ struct PartialParams {
   int32_t mode;       // SplitMode
   int32_t num_wg;     // W
   int32_t num_splits; // S (SPLIT_FIXED)
+  int64_t total_pages; // P from the plan's host copy of seq_lens (SPLIT_BALANCED)
   float score_scale;  // softmax_scale * log2(e) * kv_scale: scores in log2 units
   float v_scale;      // kv_scale applied to the value rows (1 for bf16)
 };
@@ -94,6 +112,7 @@ struct MergeParams {
   // MERGE_DECODE: groups = batch, slot ranges from the split closed forms
   const int32_t* seq_lens;
   int32_t batch, max_pages, split_mode, num_wg, num_splits;
+  int64_t total_pages;    // P of the plan (SPLIT_BALANCED)
 };
 
 }  // namespace mla

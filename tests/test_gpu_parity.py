@@ -374,3 +374,74 @@ def test_out_of_range_page_gives_nan_not_fault():
     assert np.isnan(l[1]).all() and np.isnan(o[1]).all()
     o_ref, l_ref = run_oracle(wl, requests=[0, 2])
     compare(wl, o[[0, 2]], l[[0, 2]], o_ref, l_ref, "other requests")
+
+
+# ------------------------------------------------------------ launch paths
+
+@pytest.mark.parametrize("name,splits", [("long32k", 0), ("long32k", 16), ("tiny", 4)])
+def test_single_and_two_launch_paths_agree(name, splits, monkeypatch):
+    """The single-launch kernel (stages meeting at a device-wide barrier) and the two
+    back-to-back kernels give bit-identical results."""
+    wl = wk.make_workload(name)
+    a = run_gpu(wl, num_splits=splits)
+    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "0")
+    b = run_gpu(wl, num_splits=splits)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    o_ref, l_ref = run_oracle(wl)
+    compare(wl, b[0], b[1], o_ref, l_ref, f"two launches, splits={splits}")
+
+
+def test_repeated_calls_reuse_control_words():
+    """Many calls on one workspace: the barrier words are left ready each time."""
+    import torch
+
+    wl = wk.make_workload(None, seed=601, batch=2, q_len=1, num_heads=16, seq_lens=[5000, 300])
+    dev = wk.to_device(wl)
+    plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale)
+    ws = mb.workspace(plan)
+    out = torch.empty((2, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((2, 1, 16), dtype=torch.float32, device="cuda")
+    kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], mb.MLA_BF16)
+    first = None
+    for _ in range(50):
+        mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    o_ref, l_ref = run_oracle(wl)
+    compare(wl, o.astype(np.float64), l.astype(np.float64), o_ref, l_ref, "50th call")
+    words = ws[:16].view(torch.int32).cpu().numpy()
+    assert words[0] == 0 and words[2] == 0x4D4C4131
+
+
+def test_uninitialised_workspace_gives_nan_not_hang():
+    import torch
+
+    wl = wk.make_workload(None, seed=602, batch=1, q_len=1, num_heads=16, seq_lens=[3000])
+    dev = wk.to_device(wl)
+    plan = mb.Plan(1, 1, 16, wl.seq_lens, wl.softmax_scale)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")  # no init
+    out = torch.empty((1, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 1, 16), dtype=torch.float32, device="cuda")
+    kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], mb.MLA_BF16)
+    mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(lse).all() and torch.isnan(out.float()).all()
+    mb.workspace_init(plan, ws)
+    mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all()
+
+
+def test_device_lengths_disagreeing_with_plan_give_nan():
+    import torch
+
+    wl = wk.make_workload(None, seed=603, batch=2, q_len=1, num_heads=16, seq_lens=[700, 700])
+    dev = wk.to_device(wl)
+    plan = mb.Plan(2, 1, 16, [700, 500], wl.softmax_scale)  # host copy differs
+    ws = mb.workspace(plan)
+    out = torch.empty((2, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((2, 1, 16), dtype=torch.float32, device="cuda")
+    kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], mb.MLA_BF16)
+    mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(lse).all()
