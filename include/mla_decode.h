@@ -169,10 +169,10 @@ int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity);
  * in the workspace: fp32 O [num_parts][q_len*num_heads][512] at byte 256, then fp32 LSE
  * [num_parts][q_len*num_heads] at the next 256-byte boundary (rows ordered token-major,
  * then head).
- * When all of the plan's workgroups fit on the device at once, both stages run in one
- * kernel whose workgroups meet at a device-wide barrier kept in the workspace's control
- * words; otherwise (or with the environment variable MLA_SINGLE_LAUNCH=0) two kernels
- * run back to back.  Results are identical either way.  In the single-launch path, a
+ * By default the two stages run as two kernels back to back.  With the environment
+ * variable MLA_SINGLE_LAUNCH=1, and when all of the plan's workgroups fit on the device
+ * at once, both stages run in one kernel whose workgroups meet at a device-wide barrier
+ * kept in the workspace's control words.  Results are identical either way.  In the single-launch path, a
  * workspace whose control words were not initialised (mla_workspace_init) yields NaN
  * outputs, never a hang; a barrier wait that exceeds its bound (about 0.1 s) also
  * yields NaN and marks the control words, so later calls yield NaN until the workspace

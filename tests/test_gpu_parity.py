@@ -383,6 +383,7 @@ def test_single_and_two_launch_paths_agree(name, splits, monkeypatch):
     """The single-launch kernel (stages meeting at a device-wide barrier) and the two
     back-to-back kernels give bit-identical results."""
     wl = wk.make_workload(name)
+    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "1")
     a = run_gpu(wl, num_splits=splits)
     monkeypatch.setenv("MLA_SINGLE_LAUNCH", "0")
     b = run_gpu(wl, num_splits=splits)
@@ -391,10 +392,11 @@ def test_single_and_two_launch_paths_agree(name, splits, monkeypatch):
     compare(wl, b[0], b[1], o_ref, l_ref, f"two launches, splits={splits}")
 
 
-def test_repeated_calls_reuse_control_words():
+def test_repeated_calls_reuse_control_words(monkeypatch):
     """Many calls on one workspace: the barrier words are left ready each time."""
     import torch
 
+    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "1")
     wl = wk.make_workload(None, seed=601, batch=2, q_len=1, num_heads=16, seq_lens=[5000, 300])
     dev = wk.to_device(wl)
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale)
@@ -413,9 +415,10 @@ def test_repeated_calls_reuse_control_words():
     assert words[0] == 0 and words[2] == 0x4D4C4131
 
 
-def test_uninitialised_workspace_gives_nan_not_hang():
+def test_uninitialised_workspace_gives_nan_not_hang(monkeypatch):
     import torch
 
+    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "1")
     wl = wk.make_workload(None, seed=602, batch=1, q_len=1, num_heads=16, seq_lens=[3000])
     dev = wk.to_device(wl)
     plan = mb.Plan(1, 1, 16, wl.seq_lens, wl.softmax_scale)
