@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=240)
     ap.add_argument("--workload", default="long32k")
     ap.add_argument("--splits", default="auto")
+    ap.add_argument("--partial", default="fp32", choices=["bf16", "fp32"],
+                    help="storage type of the partial answers between the two kernels")
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--repeats", type=int, default=5)
@@ -146,7 +148,8 @@ def main():
 
     t_plan = time.perf_counter()
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
-                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype)
+                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype,
+                   partials_bf16=args.partial == "bf16")
     t_plan = time.perf_counter() - t_plan
     ws = mb.workspace(plan)
     B, T, H = wl.batch, wl.q_len, wl.num_heads
@@ -230,7 +233,7 @@ def main():
             "workload": describe(wl, splits),
             "batch": B, "q_len": T, "num_heads": H, "seq_len": int(wl.seq_lens.max()),
             "kv_dtype": wl.kv_format, "splits": "auto" if splits == 0 else splits,
-            "layers_rotated": nl, "launch": args.mode,
+            "layers_rotated": nl, "launch": args.mode, "partials": args.partial,
         },
         "us_per_layer_step": round(ms * 1e3, 3),
         "pct_of_8TBs": round(100 * gbs / HBM_PEAK_GBS, 2),

@@ -86,7 +86,11 @@ typedef enum {
  *   block_table int32 [batch][max_pages_per_seq], physical page ids.  Only the first
  *               ceil(seq_lens[r]/page_size) entries of row r are read.
  *   seq_lens    int32 [batch], cached positions per request including its q_len query
- *               tokens.  Must equal the host copy the plan was made from.
+ *               tokens.  Must equal the host copy the plan was made from: the merge
+ *               stage compares them, and a request whose device length differs comes out
+ *               as NaN rows (for batch <= 64 per request; above that, a total page count
+ *               that differs makes every row NaN).  The partial stage works from the
+ *               plan's copy (batch <= 64) and does not check.
  */
 typedef struct {
   const void* pool;
@@ -113,6 +117,13 @@ typedef struct {
  *                 page-aligned contiguous pieces per request (16 is the policy the
  *                 pages describe for the AITER assembly path, 1 the one-workgroup-
  *                 per-request policy of the older path)
+ *   partials_bf16 storage of the partial answers between the two stages: 0 = fp32
+ *                 (exact to fp32), 1 = bf16 (rounded to nearest even; the merge still
+ *                 computes in fp32; half the workspace traffic).  A partial answer is
+ *                 normalised, |O_p| <= max |value|, so bf16 storage moves the merged O by
+ *                 at most 2^-9 of the largest |O_p|: negligible on long histories, where
+ *                 |O| is small, but a second rounding on top of a bf16 output when a
+ *                 few positions dominate and |O| is near max |value|.
  */
 typedef struct {
   int32_t batch;
@@ -121,6 +132,7 @@ typedef struct {
   float softmax_scale;
   int32_t causal;
   int32_t num_splits;
+  int32_t partials_bf16; /* 0: fp32 partial answers, 1: bf16 */
 } mla_decode_shape;
 
 typedef struct mla_plan mla_plan; /* opaque, host memory */
@@ -157,41 +169,24 @@ int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity);
  *   q          bf16 [batch][q_len][num_heads][576], 16-byte aligned
  *   kv         paged latent KV (kv->kv_dtype must match the plan's)
  *   workspace  device scratch of at least the plan's workspace_bytes, 256-byte
- *              aligned.  Bytes [0, 256) are control words of the single-launch path
- *              (see mla_workspace_init); the rest holds the partial answers between the
- *              two stages and needs no initialisation.
+ *              aligned.  It holds the partial answers between the two stages and needs
+ *              no initialisation.
  *   out        [batch][q_len][num_heads][512] of out_dtype (MLA_BF16, rounded to
  *              nearest even, or MLA_FP32), 16-byte aligned, or NULL
  *   out_lse    fp32 [batch][q_len][num_heads] natural-log LSE, or NULL.  With it the
  *              result is a DCP shard's partial answer (section 1): merge shards with
  *              mla_merge_lse.
- * With out == NULL and out_lse == NULL only the partial stage runs; the partials stay
- * in the workspace: fp32 O [num_parts][q_len*num_heads][512] at byte 256, then fp32 LSE
- * [num_parts][q_len*num_heads] at the next 256-byte boundary (rows ordered token-major,
- * then head).
- * By default the two stages run as two kernels back to back.  With the environment
- * variable MLA_SINGLE_LAUNCH=1, and when all of the plan's workgroups fit on the device
- * at once, both stages run in one kernel whose workgroups meet at a device-wide barrier
- * kept in the workspace's control words.  Results are identical either way.  In the single-launch path, a
- * workspace whose control words were not initialised (mla_workspace_init) yields NaN
- * outputs, never a hang; a barrier wait that exceeds its bound (about 0.1 s) also
- * yields NaN and marks the control words, so later calls yield NaN until the workspace
- * is initialised again.
+ * The two stages run as two kernels back to back on `stream`.  With out == NULL and
+ * out_lse == NULL only the partial stage runs and the partials stay in the workspace:
+ * at byte 0, O of partial_dtype [rows][16][num_parts][32] (row = token * num_heads +
+ * head; the 512 columns in 16 chunks of 32, each chunk's parts contiguous); then, at the
+ * next 256-byte boundary, fp32 LSE [rows][num_parts].  The parts of request r are the
+ * slots that mla_plan_get_work lists for it.
  * Calls that share a workspace must be ordered on one stream.
  */
 mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_paged_kv* kv,
                               void* workspace, size_t workspace_bytes, void* out,
                               int32_t out_dtype, float* out_lse, void* stream);
-
-/*
- * Initialise the control words (bytes [0, 256)) of a workspace for the single-launch
- * path: once per workspace, before its first mla_decode_splitkv, whatever plans later use
- * it; every completed call leaves them ready for the next.  Enqueued on `stream` as a
- * small kernel (safe to capture in a graph).  For callers that allocate a workspace and
- * keep it; no allocation happens here.
- */
-mla_status mla_workspace_init(const mla_plan* plan, void* workspace, size_t workspace_bytes,
-                              void* stream);
 
 /*
  * Merge partial answers that carry their LSE (section 1, DCP8 paragraph; section 4,

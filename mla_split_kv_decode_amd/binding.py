@@ -52,6 +52,7 @@ class MlaDecodeShape(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
+        ("partials_bf16", ctypes.c_int32),
     ]
 
 
@@ -68,7 +69,6 @@ def _signatures():
         "mla_decode_splitkv": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_size_t, P, c.c_int32,
                                          P, P]),
         "mla_merge_lse": (c.c_int, [P, c.c_int32, P, c.c_int32, c.c_int64, P, c.c_int32, P, P]),
-        "mla_workspace_init": (c.c_int, [P, P, c.c_size_t, P]),
         "mla_block_table_check": (c.c_int, [P, c.c_int32, c.c_int32, P, c.c_int32, c.c_int64]),
         "mla_page_bytes": (c.c_size_t, [c.c_int32, c.c_int32]),
         "mla_status_str": (c.c_char_p, [c.c_int]),
@@ -140,10 +140,11 @@ class Plan:
     """A decode plan (host object): partition of the histories into workgroup pieces."""
 
     def __init__(self, batch, q_len, num_heads, seq_lens_host, softmax_scale, causal=True,
-                 num_splits=0, kv_dtype=MLA_BF16, num_cus=0, page_size=PAGE_SIZE):
+                 num_splits=0, kv_dtype=MLA_BF16, num_cus=0, page_size=PAGE_SIZE,
+                 partials_bf16=False):
         lib = load()
         self.shape = MlaDecodeShape(int(batch), int(q_len), int(num_heads), float(softmax_scale),
-                                    int(bool(causal)), int(num_splits))
+                                    int(bool(causal)), int(num_splits), int(bool(partials_bf16)))
         sl = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
         assert sl.shape == (batch,)
         h = ctypes.c_void_p()
@@ -190,18 +191,11 @@ def paged_kv(pool, block_table, seq_lens, kv_dtype, kv_scale=1.0, page_size=PAGE
                       _ptr(seq_lens))
 
 
-def workspace(plan, device="cuda", stream=None):
-    """A device workspace for `plan`, its control words initialised."""
+def workspace(plan, device="cuda"):
+    """A device workspace for `plan` (no initialisation needed)."""
     import torch
 
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=device)
-    workspace_init(plan, ws, stream)
-    return ws
-
-
-def workspace_init(plan, ws, stream=None):
-    _check(load().mla_workspace_init(plan.handle, _ptr(ws), ws.numel() * ws.element_size(),
-                                     _stream(stream)))
+    return torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=device)
 
 
 def decode_splitkv(plan, q, kv, ws, out=None, out_dtype=MLA_BF16, out_lse=None, stream=None):

@@ -16,11 +16,8 @@
 
 namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream);
-hipError_t launch_merge(const MergeParams& p, int64_t total_rows, hipStream_t stream);
-hipError_t launch_fused(const PartialParams& p, const MergeParams& mp, uint32_t* ctrl, bool fp8,
-                        hipStream_t stream, bool* launched);
-hipError_t launch_init_ctrl(uint32_t* w, hipStream_t stream);
-int partial_waves_per_row_block(int row_blocks);
+hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
+                        hipStream_t stream);
 size_t partial_lds_size(bool fp8, int row_blocks);
 }  // namespace mla
 
@@ -38,8 +35,10 @@ struct mla_plan {
   int32_t num_wg;        // workgroups of the partial stage
   int32_t num_splits;    // S (SPLIT_FIXED)
   int32_t num_slots;     // partial answers the workspace holds
+  int32_t part_bf16;     // partial O element type
   int64_t total_pages;
-  size_t ctrl_offset, o_offset, o_bytes, lse_offset, workspace_bytes;
+  int32_t max_req_pages;  // largest ceil(seq_len / page) of a request
+  size_t o_offset, o_bytes, lse_offset, workspace_bytes;
   std::vector<int32_t> seq_lens;  // host copy, for get_work only
 };
 
@@ -66,6 +65,21 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The plan's lengths for the kernel arguments (only for batches that fit).
+void fill_plan_args(const mla_plan& pl, PlanArgs* a) {
+  memset(a, 0, sizeof(*a));
+  const int32_t B = pl.shape.batch;
+  if (B > kArgBatch || pl.total_pages > INT32_MAX) return;
+  a->n = B;
+  int32_t pre = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    a->len[r] = pl.seq_lens[r];
+    a->pre[r] = pre;
+    pre += pages_of(pl.seq_lens[r], INT32_MAX);
+  }
+  a->pre[B] = pre;
+}
+
 // Workgroups per compute unit the partial stage can keep resident (LDS bound).
 int wg_per_cu(bool fp8, int row_blocks) {
   const size_t lds = partial_lds_size(fp8, row_blocks);
@@ -74,19 +88,11 @@ int wg_per_cu(bool fp8, int row_blocks) {
   return n < 1 ? 1 : (n > 2 ? 2 : n);
 }
 
-// The single-launch path is taken only with MLA_SINGLE_LAUNCH=1 (read on every call):
-// its device-wide barrier costs more than the second launch it saves at the measured
-// shapes, so the two back-to-back kernels are the default.
-bool fused_enabled() {
-  const char* v = getenv("MLA_SINGLE_LAUNCH");
-  return v && v[0] == '1';
-}
-
 }  // namespace
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.2.0 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.3.0 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -141,6 +147,8 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
   if (s.causal != 0 && s.causal != 1) return fail(MLA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   if (s.num_splits < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (s.partials_bf16 != 0 && s.partials_bf16 != 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "partials_bf16 must be 0 or 1");
   if (page_size != kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (only %d)", page_size, kPage);
   if (kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3FN)
     return fail(MLA_ERR_UNSUPPORTED, "kv_dtype %d", kv_dtype);
@@ -150,10 +158,13 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
     return fail(MLA_ERR_UNSUPPORTED, "q_len * ceil(num_heads/16) = %lld > %d", (long long)row_blocks,
                 kMaxRowBlocks);
   int64_t total_pages = 0;
+  int32_t max_req_pages = 0;
   for (int32_t r = 0; r < s.batch; ++r) {
     if (seq_lens_host[r] < s.q_len)
       return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d < q_len %d", r, seq_lens_host[r], s.q_len);
-    total_pages += ((int64_t)seq_lens_host[r] + kPage - 1) / kPage;
+    const int32_t pg = pages_of(seq_lens_host[r], INT32_MAX);
+    total_pages += pg;
+    if (pg > max_req_pages) max_req_pages = pg;
   }
   if (num_cus == 0) {
     int dev = 0;
@@ -173,6 +184,7 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   pl->row_blocks = (int32_t)row_blocks;
   pl->rows = s.q_len * s.num_heads;
   pl->total_pages = total_pages;
+  pl->max_req_pages = max_req_pages;
   pl->seq_lens.assign(seq_lens_host, seq_lens_host + s.batch);
   const bool fp8 = kv_dtype == MLA_FP8_E4M3FN;
   int64_t wg, slots;
@@ -196,11 +208,10 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   }
   pl->num_wg = (int32_t)wg;
   pl->num_slots = (int32_t)slots;
-  // [control words | fp32 partial O | fp32 partial LSE]; the control words sit at byte 0
-  // for every plan, so one initialisation serves a workspace whatever plan uses it.
-  pl->ctrl_offset = 0;
-  pl->o_offset = kCtrlBytes;
-  pl->o_bytes = align256((size_t)slots * pl->rows * kDV * sizeof(float));
+  pl->part_bf16 = s.partials_bf16;
+  // [partial O | fp32 partial LSE], each 256-byte aligned
+  pl->o_offset = 0;
+  pl->o_bytes = align256((size_t)slots * pl->rows * kDV * (pl->part_bf16 ? 2 : 4));
   pl->lse_offset = pl->o_offset + pl->o_bytes;
   pl->workspace_bytes = pl->lse_offset + align256((size_t)slots * pl->rows * sizeof(float));
   if (workspace_bytes) *workspace_bytes = pl->workspace_bytes;
@@ -262,6 +273,10 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
     return fail(MLA_ERR_INVALID_ARGUMENT, "page_size %d differs from the plan's", kv->page_size);
   if (kv->num_pages < 1 || kv->max_pages_per_seq < 1)
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages and max_pages_per_seq must be >= 1");
+  if (kv->max_pages_per_seq < plan->max_req_pages)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "max_pages_per_seq %d < %d pages a request of the plan needs", kv->max_pages_per_seq,
+                plan->max_req_pages);
   const bool fp8 = kv->kv_dtype == MLA_FP8_E4M3FN;
   if (fp8) {
     if (!(kv->kv_scale > 0.f) || !std::isfinite(kv->kv_scale))
@@ -285,7 +300,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
 
   const mla_decode_shape& s = plan->shape;
   hipStream_t st = (hipStream_t)stream;
-  float* part_o = (float*)((char*)workspace + plan->o_offset);
+  void* part_o = (char*)workspace + plan->o_offset;
   float* part_lse = (float*)((char*)workspace + plan->lse_offset);
 
   PartialParams pp{};
@@ -306,10 +321,13 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   pp.mode = plan->mode;
   pp.num_wg = plan->num_wg;
   pp.num_splits = plan->num_splits;
+  pp.num_slots = plan->num_slots;
+  pp.part_bf16 = plan->part_bf16;
   pp.total_pages = plan->total_pages;
   const float log2e = 1.44269504088896341f;
   pp.score_scale = s.softmax_scale * log2e * (fp8 ? kv->kv_scale : 1.0f);
   pp.v_scale = fp8 ? kv->kv_scale : 1.0f;
+  fill_plan_args(*plan, &pp.plan);
   if (!out && !out_lse) {
     if (plan->num_wg > 0) {
       hipError_t e = launch_partial(pp, fp8, st);
@@ -324,43 +342,23 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   mp.out = out;
   mp.out_lse = out_lse;
   mp.rows = plan->rows;
-  mp.part_rows = plan->rows;
-  mp.part_bf16 = 0;
   mp.out_bf16 = out_dtype == MLA_BF16;
-  mp.mode = MERGE_DECODE;
   mp.seq_lens = kv->seq_lens;
   mp.batch = s.batch;
   mp.max_pages = kv->max_pages_per_seq;
   mp.split_mode = plan->mode;
   mp.num_wg = plan->num_wg;
   mp.num_splits = plan->num_splits;
+  mp.num_slots = plan->num_slots;
   mp.total_pages = plan->total_pages;
+  mp.plan = pp.plan;
   hipError_t e = hipSuccess;
-  if (plan->num_wg > 0 && fused_enabled()) {
-    bool launched = false;
-    uint32_t* ctrl = (uint32_t*)((char*)workspace + plan->ctrl_offset);
-    e = launch_fused(pp, mp, ctrl, fp8, st, &launched);
-    if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "fused launch: %s", hipGetErrorString(e));
-    if (launched) return ok();
-  }
   if (plan->num_wg > 0) {
     e = launch_partial(pp, fp8, st);
     if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
   }
-  e = launch_merge(mp, (int64_t)s.batch * plan->rows, st);
+  e = launch_merge(mp, plan->part_bf16, true, (int64_t)s.batch * plan->rows, st);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
-  return ok();
-}
-
-mla_status mla_workspace_init(const mla_plan* plan, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  if (!plan || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
-  if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  if (workspace_bytes < plan->workspace_bytes)
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes,
-                plan->workspace_bytes);
-  hipError_t e = launch_init_ctrl((uint32_t*)((char*)workspace + plan->ctrl_offset), (hipStream_t)stream);
-  if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "init launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -384,12 +382,9 @@ mla_status mla_merge_lse(const void* part_o, int32_t part_dtype, const float* pa
   mp.out = out;
   mp.out_lse = out_lse;
   mp.rows = rows;
-  mp.part_rows = rows;
-  mp.part_bf16 = part_dtype == MLA_BF16;
   mp.out_bf16 = out_dtype == MLA_BF16;
-  mp.mode = MERGE_GENERIC;
   mp.num_parts = num_parts;
-  hipError_t e = launch_merge(mp, rows, (hipStream_t)stream);
+  hipError_t e = launch_merge(mp, part_dtype == MLA_BF16, false, rows, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }

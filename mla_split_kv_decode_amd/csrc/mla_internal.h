@@ -41,12 +41,13 @@ constexpr int kMaxRowBlocks = 8;   // q_len * ceil(heads / 16) limit of one work
 
 enum SplitMode : int32_t { SPLIT_BALANCED = 0, SPLIT_FIXED = 1 };
 
-// Control words at the end of the workspace (fused launch): [0] barrier arrivals,
-// [1] barrier generation, [2] marker that the words were initialised.
-constexpr int kCtrlWords = 4;
-constexpr int kCtrlMagicWord = 2;
-constexpr uint32_t kCtrlMagic = 0x4D4C4131u;
-constexpr size_t kCtrlBytes = 256;
+// Partial answers between the two stages, in the workspace (slots = the plan's parts):
+//   O   [rows][kDV / kMergeCols chunks][slots][kMergeCols] of the partial element type
+//   LSE [rows][slots] fp32
+// rows = q_len * num_heads, token-major then head; request r's pieces use its own slot
+// range.  A merge unit (row, column chunk) of a request thus reads one contiguous block.
+constexpr int kMergeCols = 32;
+constexpr int kMergeChunks = kDV / kMergeCols;  // 16
 
 // Pages request r reads, from its length and the block-table row length.
 MLA_HD int32_t pages_of(int32_t seq_len, int32_t max_pages) {
@@ -64,15 +65,32 @@ MLA_HD int64_t div_floor(int64_t x, int64_t y) {
   return q;
 }
 
+// floor(x / y) as above, with plain 32-bit division when the operands fit (the usual case).
+MLA_HD int64_t div_floor_fast(int64_t x, int64_t y) {
+  if (x >= 0 && x <= 0xFFFFFFFFll && y > 0 && y <= 0xFFFFFFFFll) return (int64_t)((uint32_t)x / (uint32_t)y);
+  return div_floor(x, y);
+}
+
 // First global page of workgroup w under SPLIT_BALANCED.
-MLA_HD int64_t balanced_start(int64_t w, int64_t P, int64_t W) { return div_floor(w * P, W); }
+MLA_HD int64_t balanced_start(int64_t w, int64_t P, int64_t W) { return div_floor_fast(w * P, W); }
 
 // Workgroup holding global page g under SPLIT_BALANCED (largest w with start(w) <= g).
-MLA_HD int64_t balanced_wg_of(int64_t g, int64_t P, int64_t W) { return div_floor((g + 1) * W - 1, P); }
+MLA_HD int64_t balanced_wg_of(int64_t g, int64_t P, int64_t W) { return div_floor_fast((g + 1) * W - 1, P); }
 
 MLA_HD int32_t fixed_page_begin(int32_t s, int32_t pages, int32_t S) {
   return (int32_t)(((int64_t)s * pages) / S);
 }
+
+// The plan's host copy of the lengths, in the kernel arguments when the batch is small
+// enough, so that neither kernel waits for a device load of seq_lens before its first
+// real loads.  The device seq_lens are still read, in parallel, and a request whose
+// device length differs from the plan's gives NaN rows.
+constexpr int kArgBatch = 64;
+struct PlanArgs {
+  int32_t n;                    // requests described here (0: derive from device seq_lens)
+  int32_t len[kArgBatch];       // seq_lens of the plan
+  int32_t pre[kArgBatch + 1];   // pre[r] = sum_{s<r} ceil(len[s] / kPage)
+};
 
 // Launch parameters of the partial-attention kernel.
 struct PartialParams {
@@ -80,8 +98,8 @@ struct PartialParams {
   const uint8_t* pool;        // [num_pages][64][576] of the KV element type
   const int32_t* block_table; // [B][max_pages]
   const int32_t* seq_lens;    // [B]
-  float* part_o;              // fp32 [slots][T*H][512]
-  float* part_lse;            // fp32 [slots][T*H]
+  void* part_o;               // partial O (layout above), bf16 or fp32
+  float* part_lse;            // fp32 [rows][slots]
   int64_t num_pages;
   int32_t max_pages;
   int32_t batch, q_len, num_heads, head_groups, rows;  // rows = T * H
@@ -89,30 +107,31 @@ struct PartialParams {
   int32_t mode;       // SplitMode
   int32_t num_wg;     // W
   int32_t num_splits; // S (SPLIT_FIXED)
+  int32_t num_slots;  // slot stride of the partial layout
+  int32_t part_bf16;  // partial O element type: 1 bf16, 0 fp32
   int64_t total_pages; // P from the plan's host copy of seq_lens (SPLIT_BALANCED)
   float score_scale;  // softmax_scale * log2(e) * kv_scale: scores in log2 units
   float v_scale;      // kv_scale applied to the value rows (1 for bf16)
+  PlanArgs plan;
 };
 
 // Launch parameters of the LSE merge kernel.
 enum MergeMode : int32_t { MERGE_GENERIC = 0, MERGE_DECODE = 1 };
 
 struct MergeParams {
-  const void* part_o;     // [slots][part_rows][512] fp32 or bf16
-  const float* part_lse;  // [slots][part_rows]
+  const void* part_o;     // MERGE_GENERIC: [num_parts][rows][512]; MERGE_DECODE: layout above
+  const float* part_lse;  // MERGE_GENERIC: [num_parts][rows]; MERGE_DECODE: [rows][slots]
   void* out;              // [groups * rows][512] or null
   float* out_lse;         // [groups * rows] or null
   int64_t rows;           // output rows per group (decode: T*H real rows)
-  int64_t part_rows;      // row stride of one slot
-  int32_t part_bf16;      // part_o element type: 1 bf16, 0 fp32
   int32_t out_bf16;       // out element type: 1 bf16, 0 fp32
-  int32_t mode;           // MergeMode
   // MERGE_GENERIC: slots [0, num_parts) for every row, groups = 1
   int32_t num_parts;
   // MERGE_DECODE: groups = batch, slot ranges from the split closed forms
   const int32_t* seq_lens;
-  int32_t batch, max_pages, split_mode, num_wg, num_splits;
+  int32_t batch, max_pages, split_mode, num_wg, num_splits, num_slots;
   int64_t total_pages;    // P of the plan (SPLIT_BALANCED)
+  PlanArgs plan;
 };
 
 }  // namespace mla

@@ -124,6 +124,16 @@ __device__ __forceinline__ void lds_read_pair_b128(const void* p, i32x4& a, i32x
                : "=v"(a), "=v"(b) : "v"(lds_addr(p)));
 }
 
+// A load of one int32 through the vector memory path.  Uniform loads would otherwise be
+// scalar loads, which the compiler waits for at once (they share a counter with LDS
+// traffic); the zero added here is opaque to it, so the load stays a vector load that it
+// tracks and waits for only where the value is used.
+__device__ __forceinline__ int32_t vector_load_i32(const int32_t* p) {
+  int32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return p[z];
+}
+
 // Eight FP8 E4M3FN codes (little-endian bytes of `raw`) -> eight bf16, exactly.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 raw) {
   bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false);
@@ -143,9 +153,16 @@ struct TileGeom {
 
   // LDS column of 16-byte chunk c of `row`: chunks are permuted within aligned groups
   // (8 for bf16, 4 for fp8) by an XOR with a row-dependent key.  An involution.
+  // bf16: rows 2 apart fall on the same banks (1152-byte rows), so their keys must move
+  // the 32-byte chunk pairs the transposing V^T reads take, not just swap within a pair;
+  // over 16 rows the key is a bijection on even and on odd rows, which keeps the K
+  // operand reads (one chunk of 16 rows) conflict-free as well.
+  __device__ static constexpr int key16(int row) {
+    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  }
   __device__ static __forceinline__ int swz(int row, int c) {
     if constexpr (FP8) return (c & ~3) | ((c & 3) ^ ((row >> 2) & 3));
-    else return (c & ~7) | ((c & 7) ^ ((row >> 1) & 7));
+    else return (c & ~7) | ((c & 7) ^ key16(row));
   }
   __device__ static __forceinline__ int offset(int row, int chunk) {
     return row * kRowBytes + swz(row, chunk) * 16;
@@ -185,13 +202,13 @@ struct OperandAddr {
       for (int j = 0; j < 4; ++j)
         vbase[j] = row * TG::kRowBytes + 16 * (4 * (wave_col_tile0 >> 2) + (j ^ lgrp)) + 8 * h;
     } else {
-      // K: row 16pt+lrow, chunk 4kk + lgrp; key (lrow>>1)&7
-      const int key = (lrow >> 1) & 7;
+      // K: row 16pt+lrow, chunk 4kk + lgrp; key key16(lrow)
+      const int key = TG::key16(lrow);
 #pragma unroll
       for (int e = 0; e < 2; ++e) kbase[e] = lrow * TG::kRowBytes + 16 * ((4 * e + lgrp) ^ key);
       // V^T (tr16): row 32c + 16hh + 4 lgrp + (lrow>>2), chunk 2n + ((lrow&3)>>1) with
-      // n = wave_col_tile0 + ct, byte 8(lrow&1); key (2 lgrp + (lrow>>3)) & 7
-      const int key_v = (2 * lgrp + (lrow >> 3)) & 7;
+      // n = wave_col_tile0 + ct, byte 8(lrow&1); key key16 of the row
+      const int key_v = TG::key16(4 * lgrp + (lrow >> 2));
       const int row = 4 * lgrp + (lrow >> 2);
       const int b = (lrow & 3) >> 1;
 #pragma unroll
@@ -208,14 +225,17 @@ struct OperandAddr {
 // is written by one wave-wide global_load_lds_dwordx4 in which lane l fills 16-byte slot
 // 64k + l.  Every wave issues exactly kPer operations (blocks past the end repeat the
 // last block: identical bytes to the identical place), so the per-wave count of
-// outstanding operations per page is a compile-time constant.
+// outstanding operations per page is a compile-time constant.  Rows at or past
+// `valid_rows` (the unwritten tail of a request's last page) are filled from the last
+// valid row instead: their scores are masked, so only their finiteness matters (a zero
+// softmax weight times a NaN left in the pool would still be NaN).
 template <bool FP8, int NW>
 struct PageCopy {
   using TG = TileGeom<FP8>;
   static constexpr int kPer = (TG::kDmaOps + NW - 1) / NW;
   int src_off[kPer];  // this lane's source offsets within a page, one per operation
-  int wave;
-  __device__ __forceinline__ PageCopy(int wave_, int lane) : wave(wave_) {
+  int wave, lane;
+  __device__ __forceinline__ PageCopy(int wave_, int lane_) : wave(wave_), lane(lane_) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) src_off[j] = TG::dma_src_offset(block(j) * 64 + lane);
   }
@@ -224,82 +244,210 @@ struct PageCopy {
     return k < TG::kDmaOps ? k : TG::kDmaOps - 1;
   }
   // The copies are issued as inline assembly so that the compiler neither delays LDS
-  // reads of the other tile behind them nor counts them: every wait on them is explicit
+  // reads of the other tiles behind them nor counts them: every wait on them is explicit
   // (wait_vmcnt), and they complete in issue order with the other vector-memory ops.
-  __device__ __forceinline__ void operator()(unsigned char* tile, const unsigned char* src) const {
+  __device__ __forceinline__ void operator()(unsigned char* tile, const unsigned char* src,
+                                             int valid_rows) const {
     const uint32_t base = lds_addr(tile);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
+      int off = src_off[j];
+      if (valid_rows < kPage) {
+        const int row = (block(j) * 64 + lane) / TG::kChunksPerRow;
+        if (row >= valid_rows) off -= (row - (valid_rows - 1)) * TG::kRowBytes;
+      }
       const uint32_t dst = __builtin_amdgcn_readfirstlane(base + block(j) * 1024);
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(dst), "v"(src_off[j]), "s"(src) : "memory", "m0");
+                   :: "s"(dst), "v"(off), "s"(src) : "memory", "m0");
     }
   }
+};
+
+// Copy the queries of a workgroup's RB row blocks (request r) into an LDS staging area of
+// RB x 16 rows of 576 bf16, laid out like a bf16 page tile (same chunk swizzle), so one
+// HBM read serves every wave that shares a row block.  Row i of row block rb is head
+// 16 hg + i of token t (rb = t * head_groups + hg); a padding head repeats the last real
+// head (its results are discarded).  Same operation-count rule as PageCopy.
+template <int NW, int RB>
+struct QueryCopy {
+  using TG = TileGeom<false>;
+  static constexpr int kBlocks = RB * kRowsPerBlock * TG::kRowBytes / 1024;
+  static constexpr int kPer = (kBlocks + NW - 1) / NW;
+  int wave, lane;
+  __device__ __forceinline__ QueryCopy(int wave_, int lane_) : wave(wave_), lane(lane_) {}
+  __device__ __forceinline__ void operator()(unsigned char* stage, const uint16_t* q_req,
+                                             int num_heads, int head_groups) const {
+    const uint32_t base = lds_addr(stage);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      int k = wave + NW * j;
+      k = k < kBlocks ? k : kBlocks - 1;
+      const int s = k * 64 + lane;
+      const int row = s / TG::kChunksPerRow, cs = s - row * TG::kChunksPerRow;
+      const int rb = row / kRowsPerBlock, i = row - rb * kRowsPerBlock;
+      const int t = rb / head_groups, hg = rb - t * head_groups;
+      const int head = min(hg * kRowsPerBlock + i, num_heads - 1);
+      const int off = (t * num_heads + head) * TG::kRowBytes + TG::swz(row, cs) * 16;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + k * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(dst), "v"(off), "s"(q_req) : "memory", "m0");
+    }
+  }
+};
+
+// Wait until at most n * PER of this wave's vector-memory operations are outstanding,
+// n in [0, NMAX] known only at run time (s_waitcnt takes an immediate).
+template <int PER, int NMAX>
+__device__ __forceinline__ void wait_pages(int n) {
+  static_assert(NMAX <= 4, "wait cases");
+  if (NMAX >= 4 && n >= 4) wait_vmcnt<(NMAX >= 4 ? 4 * PER : 0)>();
+  else if (NMAX >= 3 && n == 3) wait_vmcnt<(NMAX >= 3 ? 3 * PER : 0)>();
+  else if (NMAX >= 2 && n == 2) wait_vmcnt<(NMAX >= 2 ? 2 * PER : 0)>();
+  else if (NMAX >= 1 && n == 1) wait_vmcnt<PER>();
+  else wait_vmcnt<0>();
+}
+
+// Shape of the partial-attention workgroup.  RB row blocks of 16 query rows; G waves
+// share a row block (they split its positions for QK^T and its output columns for PV);
+// NG groups of RB * G waves run in lockstep on consecutive pages, each group on its own
+// page, and combine their answers at the end of a piece.
+template <bool FP8, int G_, int RB_, int NG_>
+struct PartialCfg {
+  static constexpr int G = G_, RB = RB_, NG = NG_;
+  using TG = TileGeom<FP8>;
+  static constexpr int WPG = RB * G;                // waves per group
+  static constexpr int NW = NG * WPG;               // waves per workgroup
+  static constexpr int NST = 4 / G;                 // 16-position sub-tiles of a page per wave
+  static constexpr int CT = 32 / G;                 // 16-column output tiles per wave
+  static constexpr int kTiles = FP8 ? 4 : 2;        // page tiles in LDS (147,456 bytes)
+  static constexpr int kSIF = kTiles / NG;          // steps (NG pages each) in flight
+  static constexpr int kPer = PageCopy<FP8, NW>::kPer;
+  // queries go through LDS when several waves need the same row block
+  static constexpr bool kQLds = G > 1 || NG > 1;
+  static constexpr int kQPer = kQLds ? QueryCopy<NW, RB>::kPer : 0;
+  static constexpr int kQTiles =
+      kQLds ? (QueryCopy<NW, RB>::kBlocks * 1024 + TG::kPageBytes - 1) / TG::kPageBytes : 0;
+  static constexpr int kXBytes = G > 1 ? NG * RB * 2 * 64 * 16 : 16;  // P exchange
+  static_assert(G == 1 || G == 2 || G == 4, "waves per row block");
+  static_assert(RB >= 1 && RB <= kMaxRowBlocks && NW <= 16, "workgroup shape");
+  static_assert(kTiles % NG == 0 && kQTiles < kTiles, "tile plan");
+  static_assert(kPer * kTiles + kQPer <= 63, "outstanding operations exceed vmcnt");
+  static_assert(NG == 1 || G > 1, "the group combine relies on the denominator barrier");
+};
+
+template <class C>
+struct PartialSmem {
+  using TG = typename C::TG;
+  __attribute__((aligned(1024))) unsigned char tiles[C::kTiles * TG::kPageBytes];
+  __attribute__((aligned(16))) unsigned char pbuf[C::kXBytes];  // P of a step
+  float red[C::NW * 16];   // row maxima of a step
+  float red2[C::NW * 16];  // row denominators of the epilogue
+  float xch[C::NG * C::RB * 16 * 2];
 };
 
 // Stage 1 for workgroup blockIdx.x: every piece it owns, partial answers to the workspace.
 // The device pointers are separate __restrict__ arguments: read-only, never aliased by
 // the output stores, so uniform reads (lengths, page ids) become scalar loads.
-template <bool FP8, int G, int NW>
+template <bool FP8, class C>
 __device__ __forceinline__ void partial_phase(
     const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ part_o, float* __restrict__ part_lse, unsigned char* tile0,
-    unsigned char* tile1, unsigned char* pbuf, float* red) {
+    void* __restrict__ part_o, float* __restrict__ part_lse, PartialSmem<C>& sm) {
   using TG = TileGeom<FP8>;
-  using Copy = PageCopy<FP8, NW>;
-  constexpr int RB = NW / G;                        // row blocks of the workgroup
-  constexpr int NST = 4 / G;                        // 16-position sub-tiles of a page per wave
-  constexpr int CT = 32 / G;                        // 16-column output tiles per wave
-  constexpr int kPer = Copy::kPer;                  // copy operations per wave per page
-  static_assert(RB * G == NW && RB <= kMaxRowBlocks, "wave layout");
+  using Copy = PageCopy<FP8, C::NW>;
+  constexpr int G = C::G, RB = C::RB, NG = C::NG, WPG = C::WPG, NST = C::NST, CT = C::CT;
+  constexpr int kTiles = C::kTiles, kSIF = C::kSIF, kPer = C::kPer;
+  constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
+
+  // Every scalar argument the prologue needs, fetched in one batch: the compiler would
+  // otherwise load some fields lazily inside branches, one memory round trip each, before
+  // the first page copy can be issued.
+  const int a_heads = p.num_heads, a_hgroups = p.head_groups, a_mode = p.mode;
+  const int a_nwg = p.num_wg, a_nsplits = p.num_splits, a_plan_n = p.plan.n, a_len0 = p.plan.len[0];
+  const int a_maxp = p.max_pages, a_batch = p.batch, a_qlen = p.q_len, a_causal = p.causal;
+  const int a_nslots = p.num_slots, a_pbf16 = p.part_bf16;
+  const int64_t a_total = p.total_pages, a_npages = p.num_pages;
+  const float a_sscale = p.score_scale, a_vscale = p.v_scale;
+  asm volatile("" ::"s"(a_heads), "s"(a_hgroups), "s"(a_mode), "s"(a_nwg), "s"(a_nsplits),
+               "s"(a_plan_n), "s"(a_len0), "s"(a_maxp), "s"(a_batch), "s"(a_qlen), "s"(a_causal),
+               "s"(a_nslots), "s"(a_pbf16), "s"(a_total), "s"(a_npages), "s"(a_sscale),
+               "s"(a_vscale));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int rb = wave / G, g = wave - (wave / G) * G;
-  const int t = rb / p.head_groups, hg = rb - t * p.head_groups;
+  const int grp = wave / WPG, wig = wave - grp * WPG;  // group, wave in group
+  const int rb = wig / G, g = wig - (wig / G) * G;
+  const int t = rb / a_hgroups, hg = rb - t * a_hgroups;
   const int head = hg * kRowsPerBlock + lrow;
-  const bool head_ok = head < p.num_heads;
+  const bool head_ok = head < a_heads;
   const Copy copy(wave, lane);
   const OperandAddr<FP8> addr(lrow, lgrp, g * CT);
+  unsigned char* const tiles = sm.tiles;
+  unsigned char* const pbuf = sm.pbuf;
+  float* const red = sm.red;
 
-  // One piece: request r, local pages [pb, pe), partial slot `slot`.
-  auto run_piece = [&](int r, int pb, int pe, int64_t slot) {
-    const int L = max(seq_lens[r], 0);
-    const int limit = p.causal ? L - p.q_len + t + 1 : L;  // visible: position < limit
-    const int32_t* trow = block_table + (int64_t)r * p.max_pages;
-    const int npages = pe - pb;
+  // One piece: request r of length L, local pages [pb, pe), partial slot `slot`.  With
+  // the plan's lengths in the arguments no device length is read here (a pending load of
+  // it would be waited for at the first page copy's inline assembly): the merge stage
+  // compares the device lengths with the plan's.
+  auto run_piece = [&](int r, int pb, int pe, int64_t slot, int L) {
+    const int limit = a_causal ? L - a_qlen + t + 1 : L;  // visible: position < limit
+    const int32_t* trow = block_table + (int64_t)r * a_maxp;
+    const int n = pe - pb;                   // pages of the piece
+    const int nsteps = (n + NG - 1) / NG;    // step s: page s * NG + group
     bool bad = false;
 
     // A page id outside the pool is never dereferenced: the copy reads page 0 instead
     // (keeping the per-wave operation count) and the piece's result becomes NaN.
-    auto page_src = [&](int lp) -> const unsigned char* {
+    auto issue = [&](int s, int gi) {
+      const int i = s * NG + gi;
+      if (i >= n) return;
+      const int lp = pb + i;
       int32_t id = trow[lp];
-      if ((uint64_t)(int64_t)id >= (uint64_t)p.num_pages) {
+      if ((uint64_t)(int64_t)id >= (uint64_t)a_npages) {
         bad = true;
         id = 0;
       }
-      return pool + (int64_t)id * TG::kPageBytes;
+      const int valid_rows = min(kPage, L - lp * kPage);
+      copy(tiles + ((s % kSIF) * NG + gi) * TG::kPageBytes, pool + (int64_t)id * TG::kPageBytes,
+           valid_rows);
     };
 
-    // Queries: ordinary loads issued before the page copies.  The compiler tracks them,
-    // and since it does not see the copies, its wait before their first use drains the
-    // copies too: both first pages have landed when the first page is consumed.  In
-    // exchange the queries never queue behind the page stream.  A padding row repeats
-    // the last real head: its outputs are discarded and rows are independent in every
-    // step, so its content does not matter.
+    // ---- queries and the first pages
     i32x4 qf[kDLatent / 32];
-    {
-      const int hq = head_ok ? head : p.num_heads - 1;
-      const uint16_t* qrow =
-          q_ptr + (((int64_t)r * p.q_len + t) * p.num_heads + hq) * kDLatent + lgrp * 8;
+    const uint16_t* q_req = q_ptr + (int64_t)r * a_qlen * a_heads * kDLatent;
+    if constexpr (C::kQLds) {
+      unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
+      QueryCopy<C::NW, RB>(wave, lane)(stage, q_req, a_heads, a_hgroups);
+      int early = 0;
+#pragma unroll
+      for (int ti = 0; ti < kEarlyTiles; ++ti) {
+        issue(ti / NG, ti % NG);
+        early += (ti < n) ? 1 : 0;
+      }
+      wait_pages<kPer, kEarlyTiles>(early);  // the query copies are older: all landed
+      barrier_lds();
+      const OperandAddr<false> qa(lrow, lgrp, 0);
+      const unsigned char* qb = stage + rb * kRowsPerBlock * TileGeom<false>::kRowBytes;
+#pragma unroll
+      for (int kk = 0; kk < kDLatent / 32; ++kk)
+        qf[kk] = *(const i32x4*)(qb + qa.kbase[kk & 1] + OperandAddr<false>::kstep(kk));
+      barrier_lds();  // the staging tiles are free again
+#pragma unroll
+      for (int ti = kEarlyTiles; ti < kTiles; ++ti) issue(ti / NG, ti % NG);
+    } else {
+      // One wave per row block: the page copies go out first, then the queries as
+      // ordinary loads.  The compiler waits for those at the next inline assembly (the
+      // first step's wait), so that step also waits for the prefetched pages; later steps
+      // are unaffected.  A padding row repeats the last real head.
+#pragma unroll
+      for (int ti = 0; ti < kTiles; ++ti) issue(ti / NG, ti % NG);
+      const int hq = head_ok ? head : a_heads - 1;
+      const uint16_t* qrow = q_req + ((int64_t)t * a_heads + hq) * kDLatent + lgrp * 8;
 #pragma unroll
       for (int kk = 0; kk < kDLatent / 32; ++kk) qf[kk] = *(const i32x4*)(qrow + kk * 32);
     }
-    asm volatile("" ::: "memory");  // the query loads are issued before the copies
-    if (npages > 0) copy(tile0, page_src(pb));
-    if (npages > 1) copy(tile1, page_src(pb + 1));
 
     float m = kNegInf;   // running max of this lane's row (log2 units)
     float lsum = 0.f;    // this lane's share of the running denominator
@@ -307,67 +455,107 @@ __device__ __forceinline__ void partial_phase(
 #pragma unroll
     for (int i = 0; i < CT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto process = [&](unsigned char* tile, int i) {
-      // this wave's copies of page i (and everything older) done, then everyone's
-      if (i + 1 < npages) wait_vmcnt<kPer>();
-      else wait_vmcnt<0>();
-      barrier_lds();
+    for (int s = 0; s < nsteps; ++s) {
+      // pages of steps s+1 .. s+kSIF-1 were issued after this step's: let them fly
+      wait_pages<kPer, (kSIF - 1) * NG>(min(n, (s + kSIF) * NG) - min(n, (s + 1) * NG));
+      barrier_lds();  // every wave's copies of this step have landed
+      const int i = s * NG + grp;
+      const bool has = i < n;  // uniform in the group
+      const unsigned char* tile = tiles + ((s % kSIF) * NG + grp) * TG::kPageBytes;
       const int lp = pb + i;
-      const int valid_rows = max(min(kPage, L - lp * kPage), 0);
-      if (valid_rows < kPage) {  // rows past the end hold poison: zero them (P = 0 there)
-        for (int idx = tid; idx < (kPage - valid_rows) * TG::kChunksPerRow; idx += NW * 64) {
-          const int row = valid_rows + idx / TG::kChunksPerRow;
-          const int col = idx % TG::kChunksPerRow;
-          *(i32x4*)(tile + row * TG::kRowBytes + col * 16) = i32x4{0, 0, 0, 0};
-        }
-        barrier_lds();
-      }
 
-      // ---- S^T = K Q^T for this wave's sub-tiles
-      f32x4 s[NST];
+      // ---- S^T = K Q^T for this wave's sub-tiles, scale, mask, tile max.  When registers
+      // allow (a wave with at most 8 output column tiles), the V^T operands of the first
+      // PV chunk are read right after the QK^T MFMAs are issued: they do not depend on the
+      // softmax, so those transposing LDS reads run under the MFMAs and the exchanges.
+      constexpr int kEarly = CT <= 8 ? 1 : 0;  // PV chunks whose operands are read early
+      f32x4 sv[NST];
+      bf16x8 va[2][CT];
+      auto read_v = [&](int c) {
 #pragma unroll
-      for (int u = 0; u < NST; ++u) {
-        const unsigned char* kt = tile + (g * NST + u) * 16 * TG::kRowBytes;
-        // all K operands of the sub-tile in flight before the first MFMA
-        bf16x8 kf[kDLatent / 32];
-#pragma unroll
-        for (int kk = 0; kk < kDLatent / 32; ++kk) {
-          const unsigned char* ka = kt + addr.kbase[kk & 1] + OperandAddr<FP8>::kstep(kk);
-          if constexpr (FP8) kf[kk] = fp8x8_to_bf16x8(*(const i32x2*)ka);
-          else kf[kk] = *(const bf16x8*)ka;
+        for (int ct = 0; ct < CT; ++ct) {
+          const unsigned char* va0 =
+              tile + c * 32 * TG::kRowBytes + addr.vbase[ct & 3] + OperandAddr<FP8>::vstep(ct);
+          if constexpr (FP8) {
+            va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
+          } else {
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
+            va[c][ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMAs
-        // two independent accumulation chains (even / odd k-steps)
-        f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < kDLatent / 32; kk += 2) {
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], __builtin_bit_cast(bf16x8, qf[kk]),
-                                                       a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              kf[kk + 1], __builtin_bit_cast(bf16x8, qf[kk + 1]), a1, 0, 0, 0);
-        }
-        s[u] = a0 + a1;
-      }
-
-      // ---- scale, mask, tile max
-      const int pos0 = lp * kPage;
+      };
       float mx = kNegInf;
+      if (has) {
 #pragma unroll
-      for (int u = 0; u < NST; ++u) {
+        for (int u = 0; u < NST; ++u) {
+          const unsigned char* kt = tile + (g * NST + u) * 16 * TG::kRowBytes;
+          bf16x8 kf[kDLatent / 32];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = pos0 + (g * NST + u) * 16 + lgrp * 4 + e;
-          const float v = j < limit ? s[u][e] * p.score_scale : kNegInf;
-          s[u][e] = v;
-          mx = fmaxf(mx, v);
+          for (int kk = 0; kk < kDLatent / 32; ++kk) {
+            const unsigned char* ka = kt + addr.kbase[kk & 1] + OperandAddr<FP8>::kstep(kk);
+            if constexpr (FP8) kf[kk] = fp8x8_to_bf16x8(*(const i32x2*)ka);
+            else kf[kk] = *(const bf16x8*)ka;
+          }
+          // one accumulation chain in k-step order (dependent MFMAs forward their
+          // accumulator), so that each MFMA consumes the oldest outstanding K read
+          f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < kDLatent / 32; ++kk)
+            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], __builtin_bit_cast(bf16x8, qf[kk]),
+                                                         a0, 0, 0, 0);
+          sv[u] = a0;
+          if constexpr (kEarly > 0) read_v(0);  // kEarly implies one sub-tile per wave
+          if constexpr (!FP8) {
+            // Instruction order of the sub-tile: six K reads ahead, then one MFMA per
+            // read, so LDS latency hides under the MFMAs; the early V^T reads go between
+            // the last six MFMAs.  (Left alone, the scheduler keeps only one or two reads
+            // ahead and each MFMA waits for its operand.)
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (kEarly > 0) {
+              static_assert(NST == 1 && 2 * CT == 16, "early V^T reads: one chunk, 16 reads");
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+              }
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+              }
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+            }
+          }
         }
+        const int pos0 = lp * kPage;
+#pragma unroll
+        for (int u = 0; u < NST; ++u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = pos0 + (g * NST + u) * 16 + lgrp * 4 + e;
+            const float v = j < limit ? sv[u][e] * a_sscale : kNegInf;
+            sv[u][e] = v;
+            mx = fmaxf(mx, v);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NST; ++u) sv[u] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if constexpr (G > 1) {
-        if (lgrp == 0) red[(rb * G + g) * 16 + lrow] = mx;
+        if (lgrp == 0) red[(grp * WPG + rb * G + g) * 16 + lrow] = mx;
         barrier_lds();
-        mx = lds_max_of<G>(&red[rb * G * 16 + lrow], mx);
+        mx = lds_max_of<G>(&red[(grp * WPG + rb * G) * 16 + lrow], mx);
       }
 
       // ---- online softmax update
@@ -376,12 +564,13 @@ __device__ __forceinline__ void partial_phase(
       const float alpha = exp2_fast(m - msub);  // m = -inf -> 0
       m = m_new;
       float ps = 0.f;
+      bf16x8 pf[2];
 #pragma unroll
       for (int u = 0; u < NST; ++u) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pv = exp2_fast(s[u][e] - msub);
-          s[u][e] = pv;
+          const float pv = exp2_fast(sv[u][e] - msub);
+          sv[u][e] = pv;
           ps += pv;
         }
       }
@@ -391,107 +580,173 @@ __device__ __forceinline__ void partial_phase(
 
       // ---- P^T as the B operand of the PV MFMA: slots 0-3 = positions 4*lgrp+0..3 of
       // the chunk's first 16-position sub-tile, slots 4-7 = the same of its second.
-      bf16x8 pf[2];
       if constexpr (G == 1) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          pf[c] = bf16x8{(__bf16)s[2 * c][0], (__bf16)s[2 * c][1], (__bf16)s[2 * c][2],
-                         (__bf16)s[2 * c][3], (__bf16)s[2 * c + 1][0], (__bf16)s[2 * c + 1][1],
-                         (__bf16)s[2 * c + 1][2], (__bf16)s[2 * c + 1][3]};
+          pf[c] = bf16x8{(__bf16)sv[2 * c][0], (__bf16)sv[2 * c][1], (__bf16)sv[2 * c][2],
+                         (__bf16)sv[2 * c][3], (__bf16)sv[2 * c + 1][0], (__bf16)sv[2 * c + 1][1],
+                         (__bf16)sv[2 * c + 1][2], (__bf16)sv[2 * c + 1][3]};
         }
       } else {
+        unsigned char* pb_rb = pbuf + (grp * RB + rb) * 2 * 64 * 16;
 #pragma unroll
         for (int u = 0; u < NST; ++u) {
           const int pt = g * NST + u;
-          bf16x4 v = bf16x4{(__bf16)s[u][0], (__bf16)s[u][1], (__bf16)s[u][2], (__bf16)s[u][3]};
-          *(bf16x4*)(pbuf + ((rb * 2 + (pt >> 1)) * 64 + lane) * 16 + (pt & 1) * 8) = v;
+          bf16x4 v = bf16x4{(__bf16)sv[u][0], (__bf16)sv[u][1], (__bf16)sv[u][2], (__bf16)sv[u][3]};
+          *(bf16x4*)(pb_rb + ((pt >> 1) * 64 + lane) * 16 + (pt & 1) * 8) = v;
         }
         barrier_lds();
         i32x4 p0, p1;
-        lds_read_pair_b128(pbuf + (rb * 2 * 64 + lane) * 16, p0, p1);
+        lds_read_pair_b128(pb_rb + lane * 16, p0, p1);
         pf[0] = __builtin_bit_cast(bf16x8, p0);
         pf[1] = __builtin_bit_cast(bf16x8, p1);
       }
 
-      // ---- O^T += V^T P^T over the page's two 32-position chunks; each chunk's V^T
-      // operands are read (transposing LDS reads) before its MFMAs are issued
+      // ---- O^T += V^T P^T over the page's two 32-position chunks
+      if (has) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 va[CT];
+        for (int c = 0; c < 2; ++c) {
+          if (c >= kEarly) read_v(c);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const unsigned char* va0 =
-              tile + c * 32 * TG::kRowBytes + addr.vbase[ct & 3] + OperandAddr<FP8>::vstep(ct);
-          if constexpr (FP8) {
-            va[ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
-          } else {
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
-            const bf16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
-            va[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
+          for (int ct = 0; ct < CT; ++ct)
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[ct], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct], pf[c], acc[ct], 0, 0, 0);
       }
 
-      barrier_lds();  // every wave is done with this tile
-      if (i + 2 < npages) copy(tile, page_src(pb + i + 2));
-    };
-
-    for (int i = 0; i < npages; i += 2) {
-      process(tile0, i);
-      if (i + 1 < npages) process(tile1, i + 1);
+      // The next copies into this step's tiles wait until every wave is done with them.
+      // Without copies (the last steps) no barrier is needed: the exchange buffers of the
+      // next step are written only after its own first barrier, and the epilogue uses
+      // buffers of its own (the group combine reuses the tiles only after the
+      // denominator barrier, by which every wave has finished its last V^T reads).
+      if ((s + kSIF) * NG < n) {
+        barrier_lds();
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) issue(s + kSIF, gi);
+      }
     }
 
-    // ---- epilogue: full row denominator, normalise, store the partial answer
+    // ---- epilogue: partial answers go to [row][32-column chunk][slot][32] (bf16 or fp32)
+    const int64_t orow = (int64_t)t * a_heads + head;
+    auto store_o = [&](int ct, f32x4 v) {
+      const int col = g * CT * 16 + ct * 16 + lgrp * 4;
+      const int64_t idx =
+          ((orow * kMergeChunks + (col >> 5)) * a_nslots + slot) * kMergeCols + (col & 31);
+      if (a_pbf16)
+        *(bf16x4*)((__bf16*)part_o + idx) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      else
+        *(f32x4*)((float*)part_o + idx) = v;
+    };
+    // the group's full row denominator
     float ls = lsum;
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
     if constexpr (G > 1) {
+      if (lgrp == 0) sm.red2[(grp * WPG + rb * G + g) * 16 + lrow] = ls;
       barrier_lds();
-      if (lgrp == 0) red[(rb * G + g) * 16 + lrow] = ls;
-      barrier_lds();
-      ls = lds_sum_of<G>(&red[rb * G * 16 + lrow]);
+      ls = lds_sum_of<G>(&sm.red2[(grp * WPG + rb * G) * 16 + lrow]);
     }
-    const bool empty = m == kNegInf;
-    float oscale = empty ? 0.f : p.v_scale / ls;
-    float lse = empty ? kNegInf : (m + log2_fast(ls)) * kLn2;
-    if (bad) {
-      oscale = __builtin_nanf("");
-      lse = __builtin_nanf("");
-    }
-    if (head_ok) {
-      const int64_t orow = (int64_t)t * p.num_heads + head;
-      float* dst = part_o + (slot * p.rows + orow) * kDV + g * CT * 16 + lgrp * 4;
+    if constexpr (NG == 1) {
+      const bool empty = m == kNegInf;
+      float oscale = empty ? 0.f : a_vscale / ls;
+      float lse = empty ? kNegInf : (m + log2_fast(ls)) * kLn2;
+      if (bad) {
+        oscale = __builtin_nanf("");
+        lse = __builtin_nanf("");
+      }
+      if (head_ok) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) *(f32x4*)(dst + ct * 16) = acc[ct] * oscale;
-      if (g == 0 && lgrp == 0) part_lse[slot * p.rows + orow] = lse;
+        for (int ct = 0; ct < CT; ++ct) store_o(ct, acc[ct] * oscale);
+        if (g == 0 && lgrp == 0) part_lse[orow * a_nslots + slot] = lse;
+      }
+    } else {
+      // ---- the two groups combine: (m, l) through LDS, then each wave keeps half of its
+      // output columns and receives its partner's (same row block and columns, other
+      // group) copy of that half through the now idle page tiles.
+      static_assert(NG == 2 && CT % 2 == 0, "group combine");
+      constexpr int H2 = CT / 2;
+      float* xm = sm.xch + ((grp * RB + rb) * 16 + lrow) * 2;
+      if (g == 0 && lgrp == 0) {
+        xm[0] = m;
+        xm[1] = ls;
+      }
+      float* xa = (float*)tiles;  // [wave][H2][64 lanes][4]
+#pragma unroll
+      for (int c = 0; c < H2; ++c) {
+        const f32x4 v = grp == 0 ? acc[H2 + c] : acc[c];
+        *(f32x4*)(xa + ((wave * H2 + c) * 64 + lane) * 4) = v;
+      }
+      barrier_lds();
+      const float* xo = sm.xch + (((1 - grp) * RB + rb) * 16 + lrow) * 2;
+      const float m_o = xo[0], l_o = xo[1];
+      const float M = fmaxf(m, m_o);
+      const float Msub = M == kNegInf ? 0.f : M;
+      const float a_s = exp2_fast(m - Msub), a_o = exp2_fast(m_o - Msub);
+      const float Lsum = a_s * ls + a_o * l_o;
+      const bool empty = M == kNegInf;
+      float oscale = empty ? 0.f : a_vscale / Lsum;
+      float lse = empty ? kNegInf : (M + log2_fast(Lsum)) * kLn2;
+      if (bad) {
+        oscale = __builtin_nanf("");
+        lse = __builtin_nanf("");
+      }
+      const int partner = (1 - grp) * WPG + wig;
+      const float* xp = xa + (partner * H2 * 64 + lane) * 4;
+      if (head_ok) {
+        if (grp == 0) {
+#pragma unroll
+          for (int c = 0; c < H2; ++c) {
+            const f32x4 o = *(const f32x4*)(xp + c * 64 * 4);
+            store_o(c, (acc[c] * a_s + o * a_o) * oscale);
+          }
+          if (g == 0 && lgrp == 0) part_lse[orow * a_nslots + slot] = lse;
+        } else {
+#pragma unroll
+          for (int c = 0; c < H2; ++c) {
+            const f32x4 o = *(const f32x4*)(xp + c * 64 * 4);
+            store_o(H2 + c, (acc[H2 + c] * a_s + o * a_o) * oscale);
+          }
+        }
+      }
     }
     barrier_lds();  // tiles and exchange buffers are reused by the next piece
   };
 
   const int64_t w = blockIdx.x;
-  if (p.mode == SPLIT_FIXED) {
-    const int S = p.num_splits;
+  const bool use_plan = a_plan_n > 0;  // lengths from the kernel arguments
+  if (a_mode == SPLIT_FIXED) {
+    const int S = a_nsplits;
     const int r = (int)(w / S), sp = (int)(w - (int64_t)r * S);
-    const int pages = pages_of(seq_lens[r], p.max_pages);
-    run_piece(r, fixed_page_begin(sp, pages, S), fixed_page_begin(sp + 1, pages, S), w);
+    const int L = use_plan ? (a_plan_n == 1 ? a_len0 : p.plan.len[r]) : max(seq_lens[r], 0);
+    const int pages = pages_of(L, a_maxp);
+    run_piece(r, fixed_page_begin(sp, pages, S), fixed_page_begin(sp + 1, pages, S), w, L);
+  } else if (a_plan_n == 1) {  // one request: its pages are the whole page axis
+    const int64_t gb = balanced_start(w, a_total, a_nwg), ge = balanced_start(w + 1, a_total, a_nwg);
+    run_piece(0, (int)gb, (int)ge, w, a_len0);
+  } else if (use_plan) {
+    const int64_t P = a_total;
+    const int64_t gb = balanced_start(w, P, a_nwg), ge = balanced_start(w + 1, P, a_nwg);
+    for (int r = 0; r < a_plan_n; ++r) {
+      const int64_t pre = p.plan.pre[r], nxt = p.plan.pre[r + 1];
+      if (nxt <= gb) continue;
+      if (pre >= ge) break;
+      const int L = p.plan.len[r];
+      const int64_t lo = gb > pre ? gb : pre, hi = ge < nxt ? ge : nxt;
+      run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r, L);
+    }
   } else {
     int64_t P = 0;
-    for (int r = 0; r < p.batch; ++r) P += pages_of(seq_lens[r], p.max_pages);
+    for (int r = 0; r < a_batch; ++r) P += pages_of(seq_lens[r], a_maxp);
     // Device lengths that disagree with the plan's: no piece is computed and the merge
     // writes NaN (the split below would not match the merge's slot ranges).
-    if (P == 0 || P != p.total_pages) return;
-    const int64_t gb = balanced_start(w, P, p.num_wg), ge = balanced_start(w + 1, P, p.num_wg);
+    if (P == 0 || P != a_total) return;
+    const int64_t gb = balanced_start(w, P, a_nwg), ge = balanced_start(w + 1, P, a_nwg);
     int64_t pre = 0;
-    for (int r = 0; r < p.batch && pre < ge; ++r) {
-      const int pr = pages_of(seq_lens[r], p.max_pages);
+    for (int r = 0; r < a_batch && pre < ge; ++r) {
+      const int L = max(seq_lens[r], 0);
+      const int pr = pages_of(L, a_maxp);
       const int64_t lo = gb > pre ? gb : pre;
       const int64_t hi = ge < pre + pr ? ge : pre + pr;
-      if (lo < hi) run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r);
+      if (lo < hi) run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r, L);
       pre += pr;
     }
   }
@@ -499,53 +754,92 @@ __device__ __forceinline__ void partial_phase(
 
 // ------------------------------------------------------------------- merge
 //
-// A merge unit is (output row, 32-column chunk).  Thread (part lane pl, column quad cq)
-// owns parts s0 + pl, s0 + pl + 32, ...; a round of 8 parts per lane (256 parts per unit)
-// has all its loads (O quads and LSEs) in flight together, so a merge of up to 256 parts
-// costs one memory round trip.
+// A merge unit is (output row, 32-column chunk).  Thread (slot lane sl, column piece cp)
+// owns 16 bytes of each of slots s0 + sl, s0 + sl + SPP, ...: 8 columns of bf16 parts or
+// 4 of fp32 parts.  A round of 256 slots per unit has all its loads (O pieces and LSEs)
+// in flight together, so a merge of up to 256 parts costs one memory round trip.
 
-constexpr int kMergeCols = 32;
 constexpr int kMergeThreads = 256;
-constexpr int kMergeQuads = kMergeCols / 4;            // 8
-constexpr int kMergeLanes = kMergeThreads / kMergeQuads;  // 32 part lanes
-constexpr int kMergeUnroll = 8;                        // parts per lane per round
-constexpr int kMergeRound = kMergeLanes * kMergeUnroll;   // 256
-constexpr int kMergeChunks = kDV / kMergeCols;         // 16 units per output row
+constexpr int kMergeWaves = kMergeThreads / 64;
 
 __device__ __forceinline__ float nan_max(float a, float b) {
   // a NaN LSE (a piece that met a bad page id) must reach the output
   return a != a ? a : (b != b ? b : fmaxf(a, b));
 }
 
-struct MergeScratch {
-  float m[kMergeThreads / 64];
-  f32x4 v[kMergeThreads / 64][kMergeQuads];
-  float s[kMergeThreads / 64][kMergeQuads];
+template <bool PART_BF16>
+struct MergeGeom {
+  static constexpr int kCPT = PART_BF16 ? 8 : 4;          // columns per thread
+  static constexpr int kTPS = kMergeCols / kCPT;          // threads per slot
+  static constexpr int kSPP = kMergeThreads / kTPS;       // slots per pass
+  static constexpr int kPasses = 256 / kSPP;              // passes per round of 256 slots
 };
 
-// Runs with any block of at least kMergeThreads threads; threads past kMergeThreads only
-// take part in the barriers.
-template <bool PART_BF16, bool OUT_BF16>
-__device__ __forceinline__ void merge_unit(const MergeParams& p, int64_t unit, MergeScratch& sc,
-                                           bool force_nan) {
+template <bool PART_BF16>
+__device__ __forceinline__ void load_piece(const void* base, int64_t idx, float (&v)[MergeGeom<PART_BF16>::kCPT]) {
+  if constexpr (PART_BF16) {
+    const bf16x8 b = *(const bf16x8*)((const __bf16*)base + idx);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = (float)b[c];
+  } else {
+    const f32x4 f = *(const f32x4*)((const float*)base + idx);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = f[c];
+  }
+}
+
+template <bool PART_BF16, bool OUT_BF16, bool DECODE>
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p) {
+  using MG = MergeGeom<PART_BF16>;
+  constexpr int kCPT = MG::kCPT, kTPS = MG::kTPS, kSPP = MG::kSPP, kPasses = MG::kPasses;
+  __shared__ float sm_m[kMergeWaves];
+  __shared__ float sm_acc[kMergeWaves][kTPS][kCPT];
+  __shared__ float sm_den[kMergeWaves];
+
+  // scalar arguments of the prologue in one batch (see partial_phase)
+  const int64_t a_rows = p.rows, a_total = p.total_pages;
+  const int a_nwg = p.num_wg, a_nsplits = p.num_splits, a_mode = p.split_mode, a_plan_n = p.plan.n;
+  const int a_nparts = p.num_parts, a_nslots = p.num_slots, a_len0 = p.plan.len[0];
+  asm volatile("" ::"s"(a_rows), "s"(a_total), "s"(a_nwg), "s"(a_nsplits), "s"(a_mode), "s"(a_plan_n),
+               "s"(a_nparts), "s"(a_nslots), "s"(a_len0));
+
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const bool active = tid < kMergeThreads;
-  const int pl = tid >> 3, cq = tid & 7;
+  const int sl = tid / kTPS, cp = tid - (tid / kTPS) * kTPS;
+  const int64_t unit = blockIdx.x;
   const int64_t orow = unit / kMergeChunks;
-  const int cchunk = (int)(unit - orow * kMergeChunks);
-  const int64_t grp = (int64_t)((uint32_t)orow / (uint32_t)p.rows);  // rows * groups < 2^31
-  const int64_t row = orow - grp * p.rows;
+  const int chunk = (int)(unit - orow * kMergeChunks);
+  const int64_t grp = (int64_t)((uint32_t)orow / (uint32_t)a_rows);  // rows * groups < 2^31
+  const int64_t row = orow - grp * a_rows;
 
   // slot range [s0, s1) of this group.  Under SPLIT_BALANCED every workgroup owns at
   // least one page (W <= P), so every slot in the range holds a piece.
   int64_t s0 = 0, s1 = 0;
-  bool inconsistent = force_nan;
-  if (p.mode == MERGE_GENERIC) {
-    s1 = p.num_parts;
-  } else if (p.split_mode == SPLIT_FIXED) {
-    s0 = grp * p.num_splits;
-    s1 = s0 + p.num_splits;
+  bool inconsistent = false;
+  // plan path: the device length (a vector load, waited for only where it is compared,
+  // after the partial answers have been loaded) must equal the plan's
+  int dev_len = 0, plan_len = 0;
+  if constexpr (!DECODE) {
+    s1 = a_nparts;
+  } else if (a_plan_n == 1) {  // one request
+    dev_len = vector_load_i32(p.seq_lens);
+    plan_len = a_len0;
+    s1 = a_mode == SPLIT_FIXED ? a_nsplits : a_nwg;
+  } else if (a_plan_n > 0) {
+    // slot range from the plan's lengths; the device length is only compared with it
+    dev_len = vector_load_i32(p.seq_lens + grp);
+    plan_len = p.plan.len[grp];
+    if (a_mode == SPLIT_FIXED) {
+      s0 = grp * a_nsplits;
+      s1 = s0 + a_nsplits;
+    } else {
+      const int64_t pre = p.plan.pre[grp], pr = p.plan.pre[grp + 1] - pre;
+      s0 = balanced_wg_of(pre, a_total, a_nwg) + grp;
+      s1 = balanced_wg_of(pre + pr - 1, a_total, a_nwg) + grp + 1;
+    }
+  } else if (a_mode == SPLIT_FIXED) {
+    s0 = grp * a_nsplits;
+    s1 = s0 + a_nsplits;
   } else {
     int64_t P = 0, pre = 0, pr = 0;
     for (int r = 0; r < p.batch; ++r) {
@@ -554,323 +848,223 @@ __device__ __forceinline__ void merge_unit(const MergeParams& p, int64_t unit, M
       if (r == grp) pr = pg;
       P += pg;
     }
-    inconsistent = inconsistent || P != p.total_pages;
+    inconsistent = P != p.total_pages;
     if (pr > 0 && !inconsistent) {
       s0 = balanced_wg_of(pre, P, p.num_wg) + grp;
       s1 = balanced_wg_of(pre + pr - 1, P, p.num_wg) + grp + 1;
     }
   }
-  const int64_t col = cchunk * kMergeCols + cq * 4;
-  auto load_o = [&](int64_t s) -> f32x4 {
-    const int64_t off = (s * p.part_rows + row) * kDV + col;
-    if constexpr (PART_BF16) {
-      const bf16x4 b = *(const bf16x4*)((const __bf16*)p.part_o + off);
-      return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-    } else {
-      return *(const f32x4*)((const float*)p.part_o + off);
-    }
+  const int64_t col = (int64_t)chunk * kMergeCols + cp * kCPT;
+  auto o_index = [&](int64_t s) -> int64_t {
+    if constexpr (DECODE) return ((row * kMergeChunks + chunk) * a_nslots + s) * kMergeCols + cp * kCPT;
+    else return (s * a_rows + row) * kDV + col;
+  };
+  auto lse_index = [&](int64_t s) -> int64_t {
+    if constexpr (DECODE) return row * a_nslots + s;
+    else return s * a_rows + row;
   };
 
   // first round: loads of O and LSE together
-  f32x4 o[kMergeUnroll];
-  float l[kMergeUnroll];
+  float o[kPasses][kCPT];
+  float l[kPasses];
 #pragma unroll
-  for (int u = 0; u < kMergeUnroll; ++u) {
-    const int64_t s = s0 + pl + kMergeLanes * u;
-    const bool ok = active && s < s1;
-    l[u] = ok ? p.part_lse[s * p.part_rows + row] : kNegInf;
-    o[u] = ok ? load_o(s) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kPasses; ++k) {
+    const int64_t s = s0 + sl + kSPP * k;
+    const bool ok = s < s1;
+    l[k] = ok ? p.part_lse[lse_index(s)] : kNegInf;
+    if (ok) load_piece<PART_BF16>(p.part_o, o_index(s), o[k]);
+    else {
+#pragma unroll
+      for (int c = 0; c < kCPT; ++c) o[k][c] = 0.f;
+    }
   }
-  // M over all parts (later rounds: LSEs only)
+  // M over all slots (later rounds: LSEs only)
   float mx = kNegInf;
+  inconsistent = inconsistent || dev_len != plan_len;
 #pragma unroll
-  for (int u = 0; u < kMergeUnroll; ++u) mx = nan_max(mx, l[u]);
-  if (active)
-    for (int64_t s = s0 + kMergeRound + tid; s < s1; s += kMergeThreads)
-      mx = nan_max(mx, p.part_lse[s * p.part_rows + row]);
+  for (int k = 0; k < kPasses; ++k) mx = nan_max(mx, l[k]);
+  for (int64_t s = s0 + 256 + tid; s < s1; s += kMergeThreads) mx = nan_max(mx, p.part_lse[lse_index(s)]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = nan_max(mx, __shfl_xor(mx, off));
-  if (active && lane == 0) sc.m[wave] = mx;
+  if (lane == 0) sm_m[wave] = mx;
   __syncthreads();
-  float M = sc.m[0];
+  float M = sm_m[0];
 #pragma unroll
-  for (int wv = 1; wv < kMergeThreads / 64; ++wv) M = nan_max(M, sc.m[wv]);
+  for (int wv = 1; wv < kMergeWaves; ++wv) M = nan_max(M, sm_m[wv]);
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float asum = 0.f;
-  if (active && M != kNegInf) {
+  float acc[kCPT];
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const float a = exp2_fast((l[u] - M) * kLog2e);  // empty parts: exp2(-inf) = 0
-      acc += a * o[u];
-      asum += a;
+  for (int c = 0; c < kCPT; ++c) acc[c] = 0.f;
+  float den = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) {
+      const float a = exp2_fast((l[k] - M) * kLog2e);  // empty slots: exp2(-inf) = 0
+#pragma unroll
+      for (int c = 0; c < kCPT; ++c) acc[c] += a * o[k][c];
+      den += a;
     }
-    for (int64_t base = s0 + kMergeRound; base < s1; base += kMergeRound) {
+    for (int64_t base = s0 + 256; base < s1; base += 256) {
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        const int64_t s = base + pl + kMergeLanes * u;
+      for (int k = 0; k < kPasses; ++k) {
+        const int64_t s = base + sl + kSPP * k;
         if (s >= s1) continue;
-        const float a = exp2_fast((p.part_lse[s * p.part_rows + row] - M) * kLog2e);
-        acc += a * load_o(s);
-        asum += a;
+        const float a = exp2_fast((p.part_lse[lse_index(s)] - M) * kLog2e);
+        float v[kCPT];
+        load_piece<PART_BF16>(p.part_o, o_index(s), v);
+#pragma unroll
+        for (int c = 0; c < kCPT; ++c) acc[c] += a * v[c];
+        den += a;
       }
     }
   }
-  // sum over the part lanes: 8 per wave (lanes cq + 8k), then the waves
+  // sum over the slot lanes: lanes cp + kTPS k of a wave, then the waves.  Every thread of
+  // a slot lane holds the same weights, so the denominator is summed over slot lanes only.
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int off = kTPS; off < 64; off <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
-    asum += __shfl_xor(asum, off);
+    for (int c = 0; c < kCPT; ++c) acc[c] += __shfl_xor(acc[c], off);
+    den += __shfl_xor(den, off);
   }
-  if (active && lane < kMergeQuads) {
-    sc.v[wave][cq] = acc;
-    sc.s[wave][cq] = asum;
+  if (lane < kTPS) {
+#pragma unroll
+    for (int c = 0; c < kCPT; ++c) sm_acc[wave][lane][c] = acc[c];
+    if (lane == 0) sm_den[wave] = den;
   }
   __syncthreads();
-  if (tid < kMergeQuads) {
-    f32x4 v = sc.v[0][cq];
-    float den = sc.s[0][cq];
+  if (tid < kTPS) {
+    float v[kCPT];
+    float d = sm_den[0];
 #pragma unroll
-    for (int wv = 1; wv < kMergeThreads / 64; ++wv) {
-      v += sc.v[wv][cq];
-      den += sc.s[wv][cq];
+    for (int c = 0; c < kCPT; ++c) v[c] = sm_acc[0][tid][c];
+#pragma unroll
+    for (int wv = 1; wv < kMergeWaves; ++wv) {
+#pragma unroll
+      for (int c = 0; c < kCPT; ++c) v[c] += sm_acc[wv][tid][c];
+      d += sm_den[wv];
     }
     const bool empty = M == kNegInf && !inconsistent;
-    f32x4 res = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : v * (1.0f / den);
-    if (inconsistent) res = f32x4{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
+    const float inv = 1.0f / d;
+#pragma unroll
+    for (int c = 0; c < kCPT; ++c) {
+      v[c] = empty ? 0.f : v[c] * inv;
+      if (inconsistent) v[c] = __builtin_nanf("");
+    }
     if (p.out) {
       const int64_t off = orow * kDV + col;
       if constexpr (OUT_BF16) {
-        *(bf16x4*)((__bf16*)p.out + off) =
-            bf16x4{(__bf16)res[0], (__bf16)res[1], (__bf16)res[2], (__bf16)res[3]};
+#pragma unroll
+        for (int c = 0; c < kCPT; c += 4)
+          *(bf16x4*)((__bf16*)p.out + off + c) =
+              bf16x4{(__bf16)v[c], (__bf16)v[c + 1], (__bf16)v[c + 2], (__bf16)v[c + 3]};
       } else {
-        *(f32x4*)((float*)p.out + off) = res;
+#pragma unroll
+        for (int c = 0; c < kCPT; c += 4)
+          *(f32x4*)((float*)p.out + off + c) = f32x4{v[c], v[c + 1], v[c + 2], v[c + 3]};
       }
     }
-    if (p.out_lse && cchunk == 0 && cq == 0) {
+    if (p.out_lse && chunk == 0 && tid == 0) {
       p.out_lse[orow] =
-          inconsistent ? __builtin_nanf("") : (empty ? kNegInf : M + log2_fast(den) * kLn2);
+          inconsistent ? __builtin_nanf("") : (empty ? kNegInf : M + log2_fast(d) * kLn2);
     }
   }
-  __syncthreads();  // scratch is reused by the next unit
 }
 
 // ------------------------------------------------------------------- kernels
 
-// LDS (two page tiles) caps residency at one or two workgroups per compute unit, so the
-// kernels ask for no extra occupancy: the register budget is what the block size allows.
-template <bool FP8, int G, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_partial_kernel(
+// The workgroup shape for RB row blocks (see PartialCfg): one row block uses two groups
+// of 4 waves, two row blocks two groups of 2 waves per row block, so the four SIMDs each
+// run two waves; larger counts use one wave (two for three blocks) per row block.
+template <bool FP8, int RB>
+struct CfgFor;
+template <bool FP8> struct CfgFor<FP8, 1> { using type = PartialCfg<FP8, 4, 1, 2>; };
+template <bool FP8> struct CfgFor<FP8, 2> { using type = PartialCfg<FP8, 2, 2, 2>; };
+template <bool FP8> struct CfgFor<FP8, 3> { using type = PartialCfg<FP8, 2, 3, 1>; };
+template <bool FP8> struct CfgFor<FP8, 4> { using type = PartialCfg<FP8, 1, 4, 1>; };
+template <bool FP8> struct CfgFor<FP8, 5> { using type = PartialCfg<FP8, 1, 5, 1>; };
+template <bool FP8> struct CfgFor<FP8, 6> { using type = PartialCfg<FP8, 1, 6, 1>; };
+template <bool FP8> struct CfgFor<FP8, 7> { using type = PartialCfg<FP8, 1, 7, 1>; };
+template <bool FP8> struct CfgFor<FP8, 8> { using type = PartialCfg<FP8, 1, 8, 1>; };
+
+// LDS (the page tiles) caps residency at one workgroup per compute unit; the register
+// budget is what that workgroup's waves per SIMD allow.
+template <bool FP8, class C>
+__global__ __launch_bounds__(C::NW * 64)
+__attribute__((amdgpu_waves_per_eu((C::NW + 3) / 4, (C::NW + 3) / 4))) void mla_partial_kernel(
     PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
-  using TG = TileGeom<FP8>;
-  constexpr int RB = NW / G;
-  __shared__ __attribute__((aligned(1024))) unsigned char tile0[TG::kPageBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char tile1[TG::kPageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char pbuf[G > 1 ? RB * 2 * 64 * 16 : 16];
-  __shared__ float red[RB * G * 16];
-  partial_phase<FP8, G, NW>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, tile0, tile1,
-                            pbuf, red);
+    void* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ PartialSmem<C> sm;
+  partial_phase<FP8, C>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
-// Both stages in one launch.  All workgroups are resident at once (the plan never asks for
-// more than the compute units hold), so after the partial answers are written they meet
-// at a device-wide barrier and then share the merge.  The barrier is a counter and a
-// generation word in the workspace; the last arriver resets the counter and bumps the
-// generation, which leaves the counter zero for the next call.  Waiting is bounded: a
-// workgroup that gives up writes NaN instead of its merge results.
-constexpr uint32_t kBarrierSpinLimit = 1u << 17;
-
-template <bool FP8, int G, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_fused_kernel(
-    PartialParams p, MergeParams mp, const uint16_t* __restrict__ q_ptr,
-    const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, float* part_o, float* part_lse, uint32_t* ctrl) {
-  using TG = TileGeom<FP8>;
-  constexpr int RB = NW / G;
-  __shared__ __attribute__((aligned(1024))) unsigned char tile0[TG::kPageBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char tile1[TG::kPageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char pbuf[G > 1 ? RB * 2 * 64 * 16 : 16];
-  __shared__ float red[RB * G * 16];
-  __shared__ MergeScratch msc;
-  __shared__ int timed_out;
-  partial_phase<FP8, G, NW>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, tile0, tile1,
-                            pbuf, red);
-
-  // ---- device-wide barrier
-  __syncthreads();  // this workgroup's partial stores are complete
-  if (threadIdx.x == 0) {
-    // Without the marker the counters are not known to start at zero (workspace never
-    // initialised, or a previous call gave up): nobody waits and every output is NaN.
-    if (__hip_atomic_load(&ctrl[kCtrlMagicWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
-        kCtrlMagic) {
-      timed_out = 1;
-    } else {
-    const uint32_t gen = __hip_atomic_load(&ctrl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish the partials device-wide
-    const uint32_t arrived =
-        __hip_atomic_fetch_add(&ctrl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int give_up = 0;
-    if (arrived == gridDim.x - 1) {
-      __hip_atomic_store(&ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      uint32_t n = 0;
-      while (__hip_atomic_load(&ctrl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++n == kBarrierSpinLimit) {
-          give_up = 1;
-          // the counters are now unreliable: later calls refuse to wait (NaN outputs)
-          __hip_atomic_store(&ctrl[kCtrlMagicWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every workgroup's partials
-    timed_out = give_up;
-    }
-  }
-  __syncthreads();
-  const bool force_nan = timed_out != 0;
-
-  // ---- merge units, spread over the workgroups
-  const int64_t units = (int64_t)mp.batch * mp.rows * kMergeChunks;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    if (mp.out_bf16) merge_unit<false, true>(mp, u, msc, force_nan);
-    else merge_unit<false, false>(mp, u, msc, force_nan);
-  }
-}
-
-template <bool PART_BF16, bool OUT_BF16>
-__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p) {
-  __shared__ MergeScratch msc;
-  merge_unit<PART_BF16, OUT_BF16>(p, blockIdx.x, msc, false);
-}
 
 // ------------------------------------------------------------------ launchers
 
 namespace {
 
-template <bool FP8, int G, int NW>
+template <bool FP8, class C>
 hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_partial_kernel<FP8, G, NW>), dim3(p.num_wg), dim3(NW * 64), 0, stream, p,
+  hipLaunchKernelGGL((mla_partial_kernel<FP8, C>), dim3(p.num_wg), dim3(C::NW * 64), 0, stream, p,
                      p.q, p.pool, p.block_table, p.seq_lens, p.part_o, p.part_lse);
   return hipGetLastError();
 }
 
-// Workgroups of the fused kernel one device holds at once (cached per device).
-template <bool FP8, int G, int NW>
-int fused_capacity() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mla_fused_kernel<FP8, G, NW>, NW * 64,
-                                                     0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
-  }
-  return cached[dev] > 0 ? cached[dev] : 0;
-}
-
-template <bool FP8, int G, int NW>
-hipError_t launch_fused_t(const PartialParams& p, const MergeParams& mp, uint32_t* ctrl,
-                          hipStream_t stream, bool* launched) {
-  *launched = false;
-  if (p.num_wg > fused_capacity<FP8, G, NW>()) return hipSuccess;  // caller falls back
-  hipLaunchKernelGGL((mla_fused_kernel<FP8, G, NW>), dim3(p.num_wg), dim3(NW * 64), 0, stream, p, mp,
-                     p.q, p.pool, p.block_table, p.seq_lens, p.part_o, p.part_lse, ctrl);
-  *launched = true;
-  return hipGetLastError();
-}
-
-template <bool FP8>
-hipError_t launch_partial_rb(const PartialParams& p, int rb, hipStream_t stream) {
+template <bool FP8, template <bool, class> class F, class... A>
+auto by_row_blocks(int rb, A&&... a) {
   switch (rb) {
-    case 1: return launch_partial_t<FP8, 4, 4>(p, stream);
-    case 2: return launch_partial_t<FP8, 2, 4>(p, stream);
-    case 3: return launch_partial_t<FP8, 2, 6>(p, stream);
-    case 4: return launch_partial_t<FP8, 1, 4>(p, stream);
-    case 5: return launch_partial_t<FP8, 1, 5>(p, stream);
-    case 6: return launch_partial_t<FP8, 1, 6>(p, stream);
-    case 7: return launch_partial_t<FP8, 1, 7>(p, stream);
-    case 8: return launch_partial_t<FP8, 1, 8>(p, stream);
+    case 1: return F<FP8, typename CfgFor<FP8, 1>::type>::run(a...);
+    case 2: return F<FP8, typename CfgFor<FP8, 2>::type>::run(a...);
+    case 3: return F<FP8, typename CfgFor<FP8, 3>::type>::run(a...);
+    case 4: return F<FP8, typename CfgFor<FP8, 4>::type>::run(a...);
+    case 5: return F<FP8, typename CfgFor<FP8, 5>::type>::run(a...);
+    case 6: return F<FP8, typename CfgFor<FP8, 6>::type>::run(a...);
+    case 7: return F<FP8, typename CfgFor<FP8, 7>::type>::run(a...);
+    default: return F<FP8, typename CfgFor<FP8, 8>::type>::run(a...);
   }
-  return hipErrorInvalidValue;
 }
 
-template <bool FP8>
-hipError_t launch_fused_rb(const PartialParams& p, const MergeParams& mp, uint32_t* ctrl, int rb,
-                           hipStream_t stream, bool* launched) {
-  switch (rb) {
-    case 1: return launch_fused_t<FP8, 4, 4>(p, mp, ctrl, stream, launched);
-    case 2: return launch_fused_t<FP8, 2, 4>(p, mp, ctrl, stream, launched);
-    case 3: return launch_fused_t<FP8, 2, 6>(p, mp, ctrl, stream, launched);
-    case 4: return launch_fused_t<FP8, 1, 4>(p, mp, ctrl, stream, launched);
-    case 5: return launch_fused_t<FP8, 1, 5>(p, mp, ctrl, stream, launched);
-    case 6: return launch_fused_t<FP8, 1, 6>(p, mp, ctrl, stream, launched);
-    case 7: return launch_fused_t<FP8, 1, 7>(p, mp, ctrl, stream, launched);
-    case 8: return launch_fused_t<FP8, 1, 8>(p, mp, ctrl, stream, launched);
-  }
-  *launched = false;
-  return hipErrorInvalidValue;
-}
+template <bool FP8, class C>
+struct PartialLaunch {
+  static hipError_t run(const PartialParams& p, hipStream_t s) { return launch_partial_t<FP8, C>(p, s); }
+};
+template <bool FP8, class C>
+struct PartialLds {
+  static size_t run() { return sizeof(PartialSmem<C>); }
+};
 
 }  // namespace
 
-// Waves per row block (G) for a row-block count: one row block needs 4 waves to keep
-// the four SIMDs busy, so its positions and output columns are split over G waves.
-int partial_waves_per_row_block(int row_blocks) {
-  if (row_blocks == 1) return 4;
-  if (row_blocks <= 3) return 2;
-  return 1;
-}
-
+// LDS bytes of one partial-stage workgroup, for the planner's residency estimate.
 size_t partial_lds_size(bool fp8, int row_blocks) {
-  const int G = partial_waves_per_row_block(row_blocks);
-  const size_t tiles = 2 * (size_t)kPage * kDLatent * (fp8 ? 1 : 2);
-  return tiles + (G > 1 ? row_blocks * 2 * 64 * 16 : 16) + row_blocks * G * 16 * 4 +
-         sizeof(MergeScratch) + 16;
+  if (row_blocks < 1 || row_blocks > kMaxRowBlocks) return 0;
+  return fp8 ? by_row_blocks<true, PartialLds>(row_blocks) : by_row_blocks<false, PartialLds>(row_blocks);
 }
 
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream) {
   const int rb = p.q_len * p.head_groups;
-  return fp8 ? launch_partial_rb<true>(p, rb, stream) : launch_partial_rb<false>(p, rb, stream);
+  if (rb < 1 || rb > kMaxRowBlocks) return hipErrorInvalidValue;
+  return fp8 ? by_row_blocks<true, PartialLaunch>(rb, p, stream)
+             : by_row_blocks<false, PartialLaunch>(rb, p, stream);
 }
 
-// Both stages in one launch when every workgroup fits on the device at once; *launched
-// reports whether it ran (otherwise the caller runs the two kernels).
-hipError_t launch_fused(const PartialParams& p, const MergeParams& mp, uint32_t* ctrl, bool fp8,
-                        hipStream_t stream, bool* launched) {
-  const int rb = p.q_len * p.head_groups;
-  return fp8 ? launch_fused_rb<true>(p, mp, ctrl, rb, stream, launched)
-             : launch_fused_rb<false>(p, mp, ctrl, rb, stream, launched);
-}
-
-hipError_t launch_merge(const MergeParams& p, int64_t total_rows, hipStream_t stream) {
+hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
+                        hipStream_t stream) {
   const dim3 grid((unsigned)(total_rows * kMergeChunks));
-  if (p.part_bf16) {
-    if (p.out_bf16) hipLaunchKernelGGL((mla_merge_kernel<true, true>), grid, dim3(kMergeThreads), 0, stream, p);
-    else hipLaunchKernelGGL((mla_merge_kernel<true, false>), grid, dim3(kMergeThreads), 0, stream, p);
-  } else {
-    if (p.out_bf16) hipLaunchKernelGGL((mla_merge_kernel<false, true>), grid, dim3(kMergeThreads), 0, stream, p);
-    else hipLaunchKernelGGL((mla_merge_kernel<false, false>), grid, dim3(kMergeThreads), 0, stream, p);
+  const int sel = (part_bf16 ? 4 : 0) + (p.out_bf16 ? 2 : 0) + (decode ? 1 : 0);
+  switch (sel) {
+#define MLA_MERGE_CASE(S, A, B, D) \
+    case S: hipLaunchKernelGGL((mla_merge_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, p); break;
+    MLA_MERGE_CASE(0, false, false, false)
+    MLA_MERGE_CASE(1, false, false, true)
+    MLA_MERGE_CASE(2, false, true, false)
+    MLA_MERGE_CASE(3, false, true, true)
+    MLA_MERGE_CASE(4, true, false, false)
+    MLA_MERGE_CASE(5, true, false, true)
+    MLA_MERGE_CASE(6, true, true, false)
+    MLA_MERGE_CASE(7, true, true, true)
+#undef MLA_MERGE_CASE
   }
-  return hipGetLastError();
-}
-
-// Initialise the workspace's control words: barrier counter and generation zero, the
-// marker set (graph-safe: a kernel, not a memset node).
-__global__ void mla_init_ctrl_kernel(uint32_t* w) {
-  if (threadIdx.x < kCtrlWords) w[threadIdx.x] = threadIdx.x == kCtrlMagicWord ? kCtrlMagic : 0u;
-}
-
-hipError_t launch_init_ctrl(uint32_t* w, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_init_ctrl_kernel, dim3(1), dim3(64), 0, stream, w);
   return hipGetLastError();
 }
 

@@ -63,9 +63,9 @@ def test_block_table_check(lib):
 
 
 def plan_status(batch=1, q_len=1, heads=16, seq_lens=(1024,), scale=TAU, causal=1, splits=0,
-                page=64, dtype=mb.MLA_BF16, cus=256):
+                page=64, dtype=mb.MLA_BF16, cus=256, partial=0):
     lib = mb.load()
-    shape = mb.MlaDecodeShape(batch, q_len, heads, scale, causal, splits)
+    shape = mb.MlaDecodeShape(batch, q_len, heads, scale, causal, splits, partial)
     sl = np.asarray(seq_lens, dtype=np.int32)
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
@@ -95,6 +95,9 @@ def test_plan_argument_checks():
     assert plan_status(q_len=3, heads=48, seq_lens=(100,)) == U  # 9 row blocks
     assert plan_status(q_len=8, heads=16, seq_lens=(100,)) == mb.MLA_OK
     assert plan_status(cus=-1) == E
+    assert plan_status(partial=1) == mb.MLA_OK
+    assert plan_status(partial=2) == E
+    assert plan_status(partial=-1) == E
 
 
 def _fake(addr=1 << 20):
@@ -129,6 +132,8 @@ def test_decode_argument_checks_enqueue_nothing():
     assert call(kvd=bad) == E
     bad = mb.MlaPagedKV(1 << 22, 16, 32, mb.MLA_BF16, 1.0, 1 << 21, 16, 1 << 23)
     assert call(kvd=bad) == E
+    bad = mb.MlaPagedKV(1 << 22, 16, 64, mb.MLA_BF16, 1.0, 1 << 21, 15, 1 << 23)
+    assert call(kvd=bad) == E  # 1024 positions need 16 pages per table row
     fplan = mb.Plan(1, 1, 16, [1024], TAU, kv_dtype=mb.MLA_FP8_E4M3FN, num_cus=256)
     for s in (0.0, -1.0, float("inf")):
         bad = mb.MlaPagedKV(1 << 22, 16, 64, mb.MLA_FP8_E4M3FN, s, 1 << 21, 16, 1 << 23)
@@ -221,9 +226,9 @@ def test_planner_invariants(seq_lens, cus):
     check_plan(seq_lens, splits=16, cus=cus)
 
 
-def test_workspace_size():
-    plan = mb.Plan(2, 4, 16, [500, 1000], TAU, num_cus=256)
+@pytest.mark.parametrize("partials_bf16,elem", [(True, 2), (False, 4)])
+def test_workspace_size(partials_bf16, elem):
+    plan = mb.Plan(2, 4, 16, [500, 1000], TAU, num_cus=256, partials_bf16=partials_bf16)
     rows = 4 * 16
-    need = plan.num_parts * rows * 512 * 4
-    assert plan.workspace_bytes >= need + plan.num_parts * rows * 4
-    assert plan.workspace_bytes % 256 == 0
+    o_bytes = -(-plan.num_parts * rows * 512 * elem // 256) * 256
+    assert plan.workspace_bytes == o_bytes + -(-plan.num_parts * rows * 4 // 256) * 256

@@ -34,7 +34,7 @@ def kv_dtype_of(wl):
 
 
 def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, heads=None,
-            block_table=None, pool=None, canary=False):
+            block_table=None, pool=None, canary=False, partial="fp32"):
     """Decode a workload on the GPU; returns (O fp64 [B][T][H][512], LSE fp64 [B][T][H])."""
     import torch
 
@@ -43,7 +43,8 @@ def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, head
         dev = dict(dev, block_table=torch.from_numpy(np.ascontiguousarray(block_table)).cuda())
     splits = wl.num_splits if num_splits is None else num_splits
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
-                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype_of(wl))
+                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype_of(wl),
+                   partials_bf16=partial == "bf16")
     ws = mb.workspace(plan)
     B, T, H = wl.batch, wl.q_len, wl.num_heads
     tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
@@ -125,10 +126,13 @@ def test_small_shapes(case):
 
 def test_fp32_output_and_no_lse():
     wl = wk.make_workload(None, seed=102, batch=2, q_len=1, num_heads=16, seq_lens=[333, 900])
-    o, l = run_gpu(wl, out_dtype="fp32")
+    o, l = run_gpu(wl, out_dtype="fp32", partial="fp32")
     o_ref, l_ref = run_oracle(wl)
-    eo, _ = compare(wl, o, l, o_ref, l_ref, "fp32 out")
-    assert eo <= 2e-3  # no final bf16 rounding
+    eo, _ = compare(wl, o, l, o_ref, l_ref, "fp32 out, fp32 partials")
+    assert eo <= 2e-3  # no bf16 rounding anywhere but P
+    o, l = run_gpu(wl, out_dtype="fp32", partial="bf16")
+    eo_b, _ = compare(wl, o, l, o_ref, l_ref, "fp32 out, bf16 partials")
+    assert eo_b <= 2e-3 + 2.0 ** -9 * 4.0  # one bf16 rounding of a part, |O_p| < 4
     o2, _ = run_gpu(wl, want_lse=False)
     assert np.abs(o2 - o_ref).max() <= TOL_O["bf16"]
 
@@ -152,9 +156,19 @@ def long32k():
     return wk.make_workload("long32k")
 
 
+@pytest.mark.parametrize("partial", ["bf16", "fp32"])
 @pytest.mark.parametrize("splits", [16, 0, 1])
-def test_long32k(long32k, splits):
-    check_full(long32k, num_splits=splits)
+def test_long32k(long32k, splits, partial):
+    check_full(long32k, num_splits=splits, partial=partial)
+
+
+def test_partial_precision_gap(long32k):
+    """On a long history bf16 partial storage moves the bf16 output by about one output
+    rounding step, and never the LSE."""
+    o16, l16 = run_gpu(long32k, num_splits=0, partial="bf16")
+    o32, l32 = run_gpu(long32k, num_splits=0, partial="fp32")
+    assert np.abs(l16 - l32).max() <= 1e-6  # LSE never goes through bf16 (summation order only)
+    assert np.abs(o16 - o32).max() <= 2e-3
 
 
 def test_long32k_seeds():
@@ -162,27 +176,30 @@ def test_long32k_seeds():
         check_full(wk.make_workload("long32k", seed=seed), num_splits=0)
 
 
-def test_ragged_sampled():
+@pytest.mark.parametrize("partial", ["fp32", "bf16"])
+def test_ragged_sampled(partial):
     wl = wk.make_workload("ragged")
-    o, l = run_gpu(wl, num_splits=0)
+    o, l = run_gpu(wl, num_splits=0, partial=partial)
     req = [0, 1, 17, 40, 63]
     o_ref, l_ref = run_oracle(wl, requests=req)
     compare(wl, o[req], l[req], o_ref, l_ref, "auto, sampled requests")
 
 
-def test_dcp_fp8_shard_sampled():
+@pytest.mark.parametrize("partial", ["fp32", "bf16"])
+def test_dcp_fp8_shard_sampled(partial):
     wl = wk.make_workload("dcp_fp8")
-    o, l = run_gpu(wl)
+    o, l = run_gpu(wl, partial=partial)
     heads = [0, 11, 12, 47, 95]
     req = [0, 3, 7]
     o_ref, l_ref = run_oracle(wl, requests=req, heads=heads)
     compare(wl, o[req][:, :, heads], l[req][:, :, heads], o_ref, l_ref, "shard, sampled")
 
 
-def test_spec_verify_sampled():
+@pytest.mark.parametrize("partial", ["fp32", "bf16"])
+def test_spec_verify_sampled(partial):
     wl = wk.make_workload("spec_verify")
-    o16, l16 = run_gpu(wl, num_splits=16)
-    o0, l0 = run_gpu(wl, num_splits=0)
+    o16, l16 = run_gpu(wl, num_splits=16, partial=partial)
+    o0, l0 = run_gpu(wl, num_splits=0, partial=partial)
     req = [0, 5]
     o_ref, l_ref = run_oracle(wl, requests=req)
     compare(wl, o16[req], l16[req], o_ref, l_ref, "16 splits, sampled")
@@ -376,75 +393,86 @@ def test_out_of_range_page_gives_nan_not_fault():
     compare(wl, o[[0, 2]], l[[0, 2]], o_ref, l_ref, "other requests")
 
 
-# ------------------------------------------------------------ launch paths
+# ------------------------------------------------------------ workspace layout
 
-@pytest.mark.parametrize("name,splits", [("long32k", 0), ("long32k", 16), ("tiny", 4)])
-def test_single_and_two_launch_paths_agree(name, splits, monkeypatch):
-    """The single-launch kernel (stages meeting at a device-wide barrier) and the two
-    back-to-back kernels give bit-identical results."""
-    wl = wk.make_workload(name)
-    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "1")
-    a = run_gpu(wl, num_splits=splits)
-    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "0")
-    b = run_gpu(wl, num_splits=splits)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    o_ref, l_ref = run_oracle(wl)
-    compare(wl, b[0], b[1], o_ref, l_ref, f"two launches, splits={splits}")
-
-
-def test_repeated_calls_reuse_control_words(monkeypatch):
-    """Many calls on one workspace: the barrier words are left ready each time."""
+@pytest.mark.parametrize("partial", ["bf16", "fp32"])
+def test_partial_only_layout(partial):
+    """With no outputs only the partial stage runs; the workspace then holds O as
+    [rows][16][parts][32] and LSE as [rows][parts], and merging each request's parts
+    (its slots from the work list) with the oracle's merge gives the oracle's answer."""
     import torch
 
-    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "1")
-    wl = wk.make_workload(None, seed=601, batch=2, q_len=1, num_heads=16, seq_lens=[5000, 300])
+    wl = wk.make_workload(None, seed=610, batch=3, q_len=2, num_heads=12, seq_lens=[900, 70, 2500])
     dev = wk.to_device(wl)
-    plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale)
+    plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale, num_splits=0,
+                   partials_bf16=partial == "bf16", num_cus=24)
     ws = mb.workspace(plan)
-    out = torch.empty((2, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((2, 1, 16), dtype=torch.float32, device="cuda")
     kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], mb.MLA_BF16)
-    first = None
-    for _ in range(50):
-        mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
+    mb.decode_splitkv(plan, dev["q"], kv, ws, out=None, out_lse=None)
     torch.cuda.synchronize()
-    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    S, rows = plan.num_parts, wl.q_len * wl.num_heads
+    elem = 2 if partial == "bf16" else 4
+    o_bytes = -(-S * rows * 512 * elem // 256) * 256
+    raw = ws[:S * rows * 512 * elem]
+    o = (raw.view(torch.bfloat16) if partial == "bf16" else raw.view(torch.float32)).float()
+    o = o.view(rows, 16, S, 32).permute(2, 0, 1, 3).reshape(S, rows, 512).cpu().numpy()
+    lse = ws[o_bytes:o_bytes + S * rows * 4].view(torch.float32).view(rows, S).T.cpu().numpy()
+    work = plan.work()
     o_ref, l_ref = run_oracle(wl)
-    compare(wl, o.astype(np.float64), l.astype(np.float64), o_ref, l_ref, "50th call")
-    words = ws[:16].view(torch.int32).cpu().numpy()
-    assert words[0] == 0 and words[2] == 0x4D4C4131
+    for r in range(wl.batch):
+        slots = work[work[:, 1] == r][:, 4]
+        om, lm = oracle.merge(o[slots].astype(np.float64), lse[slots].astype(np.float64))
+        compare(wl, om.reshape(1, wl.q_len, wl.num_heads, 512), lm.reshape(1, wl.q_len, wl.num_heads),
+                o_ref[r:r + 1], l_ref[r:r + 1], f"request {r} from {len(slots)} workspace parts")
 
 
-def test_uninitialised_workspace_gives_nan_not_hang(monkeypatch):
-    import torch
-
-    monkeypatch.setenv("MLA_SINGLE_LAUNCH", "1")
-    wl = wk.make_workload(None, seed=602, batch=1, q_len=1, num_heads=16, seq_lens=[3000])
-    dev = wk.to_device(wl)
-    plan = mb.Plan(1, 1, 16, wl.seq_lens, wl.softmax_scale)
-    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")  # no init
-    out = torch.empty((1, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((1, 1, 16), dtype=torch.float32, device="cuda")
-    kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], mb.MLA_BF16)
-    mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
-    torch.cuda.synchronize()
-    assert torch.isnan(lse).all() and torch.isnan(out.float()).all()
-    mb.workspace_init(plan, ws)
-    mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
-    torch.cuda.synchronize()
-    assert torch.isfinite(lse).all()
-
-
-def test_device_lengths_disagreeing_with_plan_give_nan():
+@pytest.mark.parametrize("splits", [0, 3])
+def test_device_lengths_disagreeing_with_plan_give_nan(splits):
+    """Up to 64 requests the kernels take the plan's lengths from their arguments and
+    compare each request's device length with it: a differing request is NaN, the
+    others are unaffected."""
     import torch
 
     wl = wk.make_workload(None, seed=603, batch=2, q_len=1, num_heads=16, seq_lens=[700, 700])
     dev = wk.to_device(wl)
-    plan = mb.Plan(2, 1, 16, [700, 500], wl.softmax_scale)  # host copy differs
+    plan = mb.Plan(2, 1, 16, [700, 500], wl.softmax_scale, num_splits=splits)  # request 1 differs
     ws = mb.workspace(plan)
     out = torch.empty((2, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((2, 1, 16), dtype=torch.float32, device="cuda")
     kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], mb.MLA_BF16)
+    mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(lse[1]).all() and torch.isnan(out[1].float()).all()
+    o_ref, l_ref = run_oracle(wl, requests=[0])
+    compare(wl, out[:1].float().cpu().numpy().astype(np.float64),
+            lse[:1].cpu().numpy().astype(np.float64), o_ref, l_ref, "consistent request")
+
+
+def test_large_batch_device_lengths_path():
+    """Past 64 requests the lengths come from the device (no plan copy in the kernel
+    arguments): results match the oracle, and a total page count that differs from the
+    plan's gives NaN everywhere."""
+    import torch
+
+    B = 70
+    rng = np.random.default_rng(604)
+    lens = rng.integers(1, 300, size=B)
+    wl = wk.make_workload(None, seed=604, batch=B, q_len=1, num_heads=16, seq_lens=list(lens),
+                          shuffled=True)
+    o, l = run_gpu(wl, num_splits=0)
+    req = [0, 33, 64, 65, 69]
+    o_ref, l_ref = run_oracle(wl, requests=req)
+    compare(wl, o[req], l[req], o_ref, l_ref, "70 requests, device lengths")
+    dev = wk.to_device(wl)
+    bad = list(lens)
+    bad[5] = bad[5] + 64  # one more page on the host side
+    plan = mb.Plan(B, 1, 16, bad, wl.softmax_scale)
+    ws = mb.workspace(plan)
+    out = torch.empty((B, 1, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, 1, 16), dtype=torch.float32, device="cuda")
+    table = np.zeros((B, wl.block_table.shape[1] + 1), dtype=np.int32)
+    table[:, :-1] = np.maximum(wl.block_table, 0)
+    kv = mb.paged_kv(dev["pool"], torch.from_numpy(table).cuda(), dev["seq_lens"], mb.MLA_BF16)
     mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
     torch.cuda.synchronize()
     assert torch.isnan(lse).all()
