@@ -218,6 +218,13 @@ struct OperandAddr {
     }
   }
   __device__ static constexpr int kstep(int kk) { return (FP8 ? 64 : 128) * (kk >> 1); }
+  // kbase[e] computed from e (for k-steps whose parity is known only at run time)
+  __device__ static __forceinline__ int kbase_of(int lrow, int lgrp, int e) {
+    if constexpr (FP8)
+      return lrow * TG::kRowBytes + 16 * ((2 * e + (lgrp >> 1)) ^ ((lrow >> 2) & 3)) + 8 * (lgrp & 1);
+    else
+      return lrow * TG::kRowBytes + 16 * ((4 * e + lgrp) ^ TG::key16(lrow));
+  }
   __device__ static constexpr int vstep(int ct) { return (FP8 ? 64 : 128) * (ct >> 2); }
 };
 
@@ -335,6 +342,81 @@ struct PartialCfg {
   static_assert(NG == 1 || G > 1, "the group combine relies on the denominator barrier");
 };
 
+// Every scalar argument a partial-stage prologue needs, fetched in one batch: the compiler
+// would otherwise load some fields lazily inside branches, one memory round trip each,
+// before the first page copy can be issued.
+struct HotArgs {
+  int heads, hgroups, mode, nwg, nsplits, plan_n, len0, maxp, batch, qlen, causal, nslots, pbf16;
+  int64_t total, npages;
+  float sscale, vscale;
+  __device__ __forceinline__ explicit HotArgs(const PartialParams& p)
+      : heads(p.num_heads), hgroups(p.head_groups), mode(p.mode), nwg(p.num_wg),
+        nsplits(p.num_splits), plan_n(p.plan.n), len0(p.plan.len[0]), maxp(p.max_pages),
+        batch(p.batch), qlen(p.q_len), causal(p.causal), nslots(p.num_slots), pbf16(p.part_bf16),
+        total(p.total_pages), npages(p.num_pages), sscale(p.score_scale), vscale(p.v_scale) {
+    asm volatile("" ::"s"(heads), "s"(hgroups), "s"(mode), "s"(nwg), "s"(nsplits), "s"(plan_n),
+                 "s"(len0), "s"(maxp), "s"(batch), "s"(qlen), "s"(causal), "s"(nslots), "s"(pbf16),
+                 "s"(total), "s"(npages), "s"(sscale), "s"(vscale));
+  }
+};
+
+// The pieces of workgroup blockIdx.x (mla_internal.h): run(r, first page, end page, slot, L)
+// for each, from the plan's lengths in the arguments when present, else from seq_lens.
+template <class F>
+__device__ __forceinline__ void for_each_piece(const PartialParams& p, const HotArgs& a,
+                                               const int32_t* __restrict__ seq_lens, F&& run_piece) {
+  const int64_t w = blockIdx.x;
+  const bool use_plan = a.plan_n > 0;
+  if (a.mode == SPLIT_FIXED) {
+    const int S = a.nsplits;
+    const int r = (int)(w / S), sp = (int)(w - (int64_t)r * S);
+    const int L = use_plan ? (a.plan_n == 1 ? a.len0 : p.plan.len[r]) : max(seq_lens[r], 0);
+    const int pages = pages_of(L, a.maxp);
+    run_piece(r, fixed_page_begin(sp, pages, S), fixed_page_begin(sp + 1, pages, S), w, L);
+  } else if (a.plan_n == 1) {  // one request: its pages are the whole page axis
+    const int64_t gb = balanced_start(w, a.total, a.nwg), ge = balanced_start(w + 1, a.total, a.nwg);
+    run_piece(0, (int)gb, (int)ge, w, a.len0);
+  } else if (use_plan) {
+    const int64_t P = a.total;
+    const int64_t gb = balanced_start(w, P, a.nwg), ge = balanced_start(w + 1, P, a.nwg);
+    for (int r = 0; r < a.plan_n; ++r) {
+      const int64_t pre = p.plan.pre[r], nxt = p.plan.pre[r + 1];
+      if (nxt <= gb) continue;
+      if (pre >= ge) break;
+      const int L = p.plan.len[r];
+      const int64_t lo = gb > pre ? gb : pre, hi = ge < nxt ? ge : nxt;
+      run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r, L);
+    }
+  } else {
+    int64_t P = 0;
+    for (int r = 0; r < a.batch; ++r) P += pages_of(seq_lens[r], a.maxp);
+    // Device lengths that disagree with the plan's: no piece is computed and the merge
+    // writes NaN (the split below would not match the merge's slot ranges).
+    if (P == 0 || P != a.total) return;
+    const int64_t gb = balanced_start(w, P, a.nwg), ge = balanced_start(w + 1, P, a.nwg);
+    int64_t pre = 0;
+    for (int r = 0; r < a.batch && pre < ge; ++r) {
+      const int L = max(seq_lens[r], 0);
+      const int pr = pages_of(L, a.maxp);
+      const int64_t lo = gb > pre ? gb : pre;
+      const int64_t hi = ge < pre + pr ? ge : pre + pr;
+      if (lo < hi) run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r, L);
+      pre += pr;
+    }
+  }
+}
+
+// Partial answer of one row of one piece to the workspace layout of mla_internal.h:
+// four consecutive columns starting at `col`.
+__device__ __forceinline__ void store_partial(void* part_o, bool bf16, int64_t orow, int col,
+                                              int nslots, int64_t slot, f32x4 v) {
+  const int64_t idx = ((orow * kMergeChunks + (col >> 5)) * nslots + slot) * kMergeCols + (col & 31);
+  if (bf16)
+    *(bf16x4*)((__bf16*)part_o + idx) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  else
+    *(f32x4*)((float*)part_o + idx) = v;
+}
+
 template <class C>
 struct PartialSmem {
   using TG = typename C::TG;
@@ -359,19 +441,11 @@ __device__ __forceinline__ void partial_phase(
   constexpr int kTiles = C::kTiles, kSIF = C::kSIF, kPer = C::kPer;
   constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
 
-  // Every scalar argument the prologue needs, fetched in one batch: the compiler would
-  // otherwise load some fields lazily inside branches, one memory round trip each, before
-  // the first page copy can be issued.
-  const int a_heads = p.num_heads, a_hgroups = p.head_groups, a_mode = p.mode;
-  const int a_nwg = p.num_wg, a_nsplits = p.num_splits, a_plan_n = p.plan.n, a_len0 = p.plan.len[0];
-  const int a_maxp = p.max_pages, a_batch = p.batch, a_qlen = p.q_len, a_causal = p.causal;
-  const int a_nslots = p.num_slots, a_pbf16 = p.part_bf16;
-  const int64_t a_total = p.total_pages, a_npages = p.num_pages;
-  const float a_sscale = p.score_scale, a_vscale = p.v_scale;
-  asm volatile("" ::"s"(a_heads), "s"(a_hgroups), "s"(a_mode), "s"(a_nwg), "s"(a_nsplits),
-               "s"(a_plan_n), "s"(a_len0), "s"(a_maxp), "s"(a_batch), "s"(a_qlen), "s"(a_causal),
-               "s"(a_nslots), "s"(a_pbf16), "s"(a_total), "s"(a_npages), "s"(a_sscale),
-               "s"(a_vscale));
+  const HotArgs args(p);
+  const int a_heads = args.heads, a_hgroups = args.hgroups, a_maxp = args.maxp;
+  const int a_qlen = args.qlen, a_causal = args.causal, a_nslots = args.nslots, a_pbf16 = args.pbf16;
+  const int64_t a_npages = args.npages;
+  const float a_sscale = args.sscale, a_vscale = args.vscale;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -628,13 +702,7 @@ __device__ __forceinline__ void partial_phase(
     // ---- epilogue: partial answers go to [row][32-column chunk][slot][32] (bf16 or fp32)
     const int64_t orow = (int64_t)t * a_heads + head;
     auto store_o = [&](int ct, f32x4 v) {
-      const int col = g * CT * 16 + ct * 16 + lgrp * 4;
-      const int64_t idx =
-          ((orow * kMergeChunks + (col >> 5)) * a_nslots + slot) * kMergeCols + (col & 31);
-      if (a_pbf16)
-        *(bf16x4*)((__bf16*)part_o + idx) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-      else
-        *(f32x4*)((float*)part_o + idx) = v;
+      store_partial(part_o, a_pbf16, orow, g * CT * 16 + ct * 16 + lgrp * 4, a_nslots, slot, v);
     };
     // the group's full row denominator
     float ls = lsum;
@@ -711,45 +779,258 @@ __device__ __forceinline__ void partial_phase(
     barrier_lds();  // tiles and exchange buffers are reused by the next piece
   };
 
-  const int64_t w = blockIdx.x;
-  const bool use_plan = a_plan_n > 0;  // lengths from the kernel arguments
-  if (a_mode == SPLIT_FIXED) {
-    const int S = a_nsplits;
-    const int r = (int)(w / S), sp = (int)(w - (int64_t)r * S);
-    const int L = use_plan ? (a_plan_n == 1 ? a_len0 : p.plan.len[r]) : max(seq_lens[r], 0);
-    const int pages = pages_of(L, a_maxp);
-    run_piece(r, fixed_page_begin(sp, pages, S), fixed_page_begin(sp + 1, pages, S), w, L);
-  } else if (a_plan_n == 1) {  // one request: its pages are the whole page axis
-    const int64_t gb = balanced_start(w, a_total, a_nwg), ge = balanced_start(w + 1, a_total, a_nwg);
-    run_piece(0, (int)gb, (int)ge, w, a_len0);
-  } else if (use_plan) {
-    const int64_t P = a_total;
-    const int64_t gb = balanced_start(w, P, a_nwg), ge = balanced_start(w + 1, P, a_nwg);
-    for (int r = 0; r < a_plan_n; ++r) {
-      const int64_t pre = p.plan.pre[r], nxt = p.plan.pre[r + 1];
-      if (nxt <= gb) continue;
-      if (pre >= ge) break;
-      const int L = p.plan.len[r];
-      const int64_t lo = gb > pre ? gb : pre, hi = ge < nxt ? ge : nxt;
-      run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r, L);
+  for_each_piece(p, args, seq_lens, run_piece);
+}
+
+
+// ------------------------------------------------------------------- K-split partial stage
+//
+// One row block of 16 query rows (one query token, up to 16 heads), eight waves per
+// workgroup, all on the same page.  In QK^T wave w computes the partial scores of the
+// 16-position sub-tile u = w & 3 over half kh = w >> 2 of the latent (nine of the 18
+// k-steps of 32 columns); the two halves are added through LDS.  In PV wave w produces
+// output columns [64 w, 64 w + 64) over the page's 64 positions.  One softmax state for the
+// whole workgroup, pages double-buffered (FP8: four in flight), and a page is processed as
+// soon as it has landed, so once the stream ends only the last page's work remains.
+template <bool FP8>
+struct KSplitCfg {
+  using TG = TileGeom<FP8>;
+  static constexpr int NW = 8;
+  static constexpr int kTiles = FP8 ? 4 : 2;
+  static constexpr int kPer = PageCopy<FP8, NW>::kPer;
+  static constexpr int KS = kDLatent / 32 / 2;  // k-steps per half: 9
+  static constexpr int CT = 4;                  // 16-column output tiles per wave
+  static constexpr int kQTiles =
+      (QueryCopy<NW, 1>::kBlocks * 1024 + TG::kPageBytes - 1) / TG::kPageBytes;
+  static_assert(kPer * kTiles + QueryCopy<NW, 1>::kPer <= 63, "outstanding operations exceed vmcnt");
+  static_assert(kQTiles < kTiles, "tile plan");
+};
+
+template <bool FP8>
+struct KSplitSmem {
+  using C = KSplitCfg<FP8>;
+  __attribute__((aligned(1024))) unsigned char tiles[C::kTiles * C::TG::kPageBytes];
+  f32x4 sx[4][64];                                               // k-half 1 partial scores
+  __attribute__((aligned(16))) unsigned char pbuf[2 * 64 * 16];  // P^T of the page, bf16
+  float red[4 * 16];                                             // row maxima of the sub-tiles
+  float red2[4 * 16];                                            // row denominators (epilogue)
+};
+
+template <bool FP8>
+__device__ __forceinline__ void partial_ks(
+    const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    void* __restrict__ part_o, float* __restrict__ part_lse, KSplitSmem<FP8>& sm) {
+  using C = KSplitCfg<FP8>;
+  using TG = TileGeom<FP8>;
+  constexpr int kTiles = C::kTiles, kPer = C::kPer, CT = C::CT, KS = C::KS;
+  constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
+  const HotArgs args(p);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int u = wave & 3, kh = wave >> 2;  // sub-tile, k-half
+  const int head = lrow;                   // one token: rows are the heads
+  const bool head_ok = head < args.heads;
+  const PageCopy<FP8, C::NW> copy(wave, lane);
+  const OperandAddr<FP8> addr(lrow, lgrp, 4 * wave);  // V^T: output column tiles 4w .. 4w+3
+  unsigned char* const tiles = sm.tiles;
+
+  auto run_piece = [&](int r, int pb, int pe, int64_t slot, int L) {
+    const int32_t* trow = block_table + (int64_t)r * args.maxp;
+    const int n = pe - pb;
+    bool bad = false;
+    // page i of the piece into tile i % kTiles; an id outside the pool is never
+    // dereferenced (page 0 is copied instead, the piece becomes NaN)
+    auto issue = [&](int i) {
+      if (i >= n) return;
+      const int lp = pb + i;
+      int32_t id = trow[lp];
+      if ((uint64_t)(int64_t)id >= (uint64_t)args.npages) {
+        bad = true;
+        id = 0;
+      }
+      copy(tiles + (i % kTiles) * TG::kPageBytes, pool + (int64_t)id * TG::kPageBytes,
+           min(kPage, L - lp * kPage));
+    };
+
+    // ---- queries through LDS (one HBM read per workgroup), then the first pages
+    unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
+    QueryCopy<C::NW, 1>(wave, lane)(stage, q_ptr + (int64_t)r * args.heads * kDLatent, args.heads, 1);
+    int early = 0;
+#pragma unroll
+    for (int ti = 0; ti < kEarlyTiles; ++ti) {
+      issue(ti);
+      early += ti < n ? 1 : 0;
     }
-  } else {
-    int64_t P = 0;
-    for (int r = 0; r < a_batch; ++r) P += pages_of(seq_lens[r], a_maxp);
-    // Device lengths that disagree with the plan's: no piece is computed and the merge
-    // writes NaN (the split below would not match the merge's slot ranges).
-    if (P == 0 || P != a_total) return;
-    const int64_t gb = balanced_start(w, P, a_nwg), ge = balanced_start(w + 1, P, a_nwg);
-    int64_t pre = 0;
-    for (int r = 0; r < a_batch && pre < ge; ++r) {
-      const int L = max(seq_lens[r], 0);
-      const int pr = pages_of(L, a_maxp);
-      const int64_t lo = gb > pre ? gb : pre;
-      const int64_t hi = ge < pre + pr ? ge : pre + pr;
-      if (lo < hi) run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r, L);
-      pre += pr;
+    wait_pages<kPer, kEarlyTiles>(early);  // the query copies are older: all landed
+    barrier_lds();
+    i32x4 qf[KS];  // this wave's half of the queries
+    {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const int kk = kh * KS + j;  // depends on the wave: offsets computed, not indexed
+        const int kb = OperandAddr<false>::kbase_of(lrow, lgrp, kk & 1);
+        qf[j] = *(const i32x4*)(stage + kb + OperandAddr<false>::kstep(kk));
+      }
     }
-  }
+    barrier_lds();  // the staging tiles are free again
+#pragma unroll
+    for (int ti = kEarlyTiles; ti < kTiles; ++ti) issue(ti);
+
+    float m = kNegInf;  // running row max (log2 units), the same in every wave
+    float lsum = 0.f;   // k-half 0 waves: this lane's share of its sub-tile's denominator
+    f32x4 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int i = 0; i < n; ++i) {
+      // pages i+1 .. i+kTiles-1 were issued after page i: let them fly
+      wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
+      barrier_lds();  // every wave's copies of page i have landed
+      const unsigned char* tile = tiles + (i % kTiles) * TG::kPageBytes;
+      const int lp = pb + i;
+
+      // ---- partial S^T of sub-tile u over this wave's k-half, then the V^T operands of
+      // this wave's output columns (both 32-position chunks; they do not depend on the
+      // softmax, so these transposing reads run under the MFMAs and the exchanges)
+      const unsigned char* kt = tile + u * 16 * TG::kRowBytes;
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const int kk = kh * KS + j;
+        const unsigned char* ka =
+            kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1) + OperandAddr<FP8>::kstep(kk);
+        if constexpr (FP8) kf[j] = fp8x8_to_bf16x8(*(const i32x2*)ka);
+        else kf[j] = *(const bf16x8*)ka;
+      }
+      f32x4 sp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], __builtin_bit_cast(bf16x8, qf[j]), sp, 0, 0, 0);
+      bf16x8 va[2][CT];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const unsigned char* va0 = tile + c * 32 * TG::kRowBytes + addr.vbase[ct] + OperandAddr<FP8>::vstep(ct);
+          if constexpr (FP8) {
+            va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
+          } else {
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
+            const bf16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
+            va[c][ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        }
+      }
+      if constexpr (!FP8) {
+        // instruction order: six K reads ahead of the MFMAs, then one MFMA per remaining
+        // read; the sixteen V^T reads go between the last six MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+
+      // ---- the k-halves meet: half 1 hands its partial scores to half 0, which scales,
+      // masks and takes its sub-tile's row max
+      if (kh == 1) sm.sx[u][lane] = sp;
+      barrier_lds();
+      f32x4 sv = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+      if (kh == 0) {
+        const f32x4 other = sm.sx[u][lane];
+        float mx = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = lp * kPage + u * 16 + lgrp * 4 + e;
+          const float v = j < L ? (sp[e] + other[e]) * args.sscale : kNegInf;
+          sv[e] = v;
+          mx = fmaxf(mx, v);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (lgrp == 0) sm.red[u * 16 + lrow] = mx;
+      }
+      barrier_lds();
+      const float mx = lds_max_of<4>(&sm.red[lrow], kNegInf);
+
+      // ---- online softmax update; half 0 builds P^T of its sub-tile for every wave
+      const float m_new = fmaxf(m, mx);
+      const float msub = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_fast(m - msub);  // m = -inf -> 0
+      m = m_new;
+      if (kh == 0) {
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = exp2_fast(sv[e] - msub);
+          ps += sv[e];
+        }
+        lsum = lsum * alpha + ps;
+        *(bf16x4*)(sm.pbuf + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
+            bf16x4{(__bf16)sv[0], (__bf16)sv[1], (__bf16)sv[2], (__bf16)sv[3]};
+      }
+      barrier_lds();
+      i32x4 p0, p1;
+      lds_read_pair_b128(sm.pbuf + lane * 16, p0, p1);
+      const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, p0), __builtin_bit_cast(bf16x8, p1)};
+
+      // ---- O^T += V^T P^T for this wave's 64 columns
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[ct], 0, 0, 0);
+      }
+
+      // the next copy into this tile waits until every wave is done with it
+      if (i + kTiles < n) {
+        barrier_lds();
+        issue(i + kTiles);
+      }
+    }
+
+    // ---- epilogue: the row denominator from the four k-half 0 waves, normalise, store
+    float ls = lsum;
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    if (kh == 0 && lgrp == 0) sm.red2[u * 16 + lrow] = ls;
+    barrier_lds();
+    ls = lds_sum_of<4>(&sm.red2[lrow]);
+    const bool empty = m == kNegInf;
+    float oscale = empty ? 0.f : args.vscale / ls;
+    float lse = empty ? kNegInf : (m + log2_fast(ls)) * kLn2;
+    if (bad) {
+      oscale = __builtin_nanf("");
+      lse = __builtin_nanf("");
+    }
+    if (head_ok) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        store_partial(part_o, args.pbf16, head, 64 * wave + 16 * ct + 4 * lgrp, args.nslots, slot,
+                      acc[ct] * oscale);
+      if (wave == 0 && lgrp == 0) part_lse[(int64_t)head * args.nslots + slot] = lse;
+    }
+    barrier_lds();  // tiles and exchange buffers are reused by the next piece
+  };
+
+  for_each_piece(p, args, seq_lens, run_piece);
 }
 
 // ------------------------------------------------------------------- merge
@@ -977,7 +1258,6 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
 // run two waves; larger counts use one wave (two for three blocks) per row block.
 template <bool FP8, int RB>
 struct CfgFor;
-template <bool FP8> struct CfgFor<FP8, 1> { using type = PartialCfg<FP8, 4, 1, 2>; };
 template <bool FP8> struct CfgFor<FP8, 2> { using type = PartialCfg<FP8, 2, 2, 2>; };
 template <bool FP8> struct CfgFor<FP8, 3> { using type = PartialCfg<FP8, 2, 3, 1>; };
 template <bool FP8> struct CfgFor<FP8, 4> { using type = PartialCfg<FP8, 1, 4, 1>; };
@@ -999,6 +1279,17 @@ __attribute__((amdgpu_waves_per_eu((C::NW + 3) / 4, (C::NW + 3) / 4))) void mla_
 }
 
 
+// One row block (one token, up to 16 heads): the K-split workgroup of eight waves.
+template <bool FP8>
+__global__ __launch_bounds__(KSplitCfg<FP8>::NW * 64)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_ks_kernel(
+    PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    void* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ KSplitSmem<FP8> sm;
+  partial_ks<FP8>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+}
+
 // ------------------------------------------------------------------ launchers
 
 namespace {
@@ -1010,10 +1301,17 @@ hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool FP8>
+hipError_t launch_partial_ks(const PartialParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_partial_ks_kernel<FP8>), dim3(p.num_wg), dim3(KSplitCfg<FP8>::NW * 64), 0,
+                     stream, p, p.q, p.pool, p.block_table, p.seq_lens, p.part_o, p.part_lse);
+  return hipGetLastError();
+}
+
+// row blocks 2 .. 8 (one row block takes the K-split kernel)
 template <bool FP8, template <bool, class> class F, class... A>
 auto by_row_blocks(int rb, A&&... a) {
   switch (rb) {
-    case 1: return F<FP8, typename CfgFor<FP8, 1>::type>::run(a...);
     case 2: return F<FP8, typename CfgFor<FP8, 2>::type>::run(a...);
     case 3: return F<FP8, typename CfgFor<FP8, 3>::type>::run(a...);
     case 4: return F<FP8, typename CfgFor<FP8, 4>::type>::run(a...);
@@ -1038,12 +1336,14 @@ struct PartialLds {
 // LDS bytes of one partial-stage workgroup, for the planner's residency estimate.
 size_t partial_lds_size(bool fp8, int row_blocks) {
   if (row_blocks < 1 || row_blocks > kMaxRowBlocks) return 0;
+  if (row_blocks == 1) return fp8 ? sizeof(KSplitSmem<true>) : sizeof(KSplitSmem<false>);
   return fp8 ? by_row_blocks<true, PartialLds>(row_blocks) : by_row_blocks<false, PartialLds>(row_blocks);
 }
 
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream) {
   const int rb = p.q_len * p.head_groups;
   if (rb < 1 || rb > kMaxRowBlocks) return hipErrorInvalidValue;
+  if (rb == 1) return fp8 ? launch_partial_ks<true>(p, stream) : launch_partial_ks<false>(p, stream);
   return fp8 ? by_row_blocks<true, PartialLaunch>(rb, p, stream)
              : by_row_blocks<false, PartialLaunch>(rb, p, stream);
 }
