@@ -33,12 +33,12 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 # rocprofv3 FETCH_SIZE / WRITE_SIZE of the partial kernel (KiB per dispatch, median) and
-# the copy-kernel calibration factors (profiles/mla_decode_<workload>_<splits>.md), keyed
-# by (workload, splits, library version): a kernel change bumps the version, so
-# `traffic` reads null until the counters are taken again.
+# the copy-kernel calibration factors (profiles/<kernel>_<workload>.md), keyed by
+# (workload, splits, partial storage, library version): a kernel change bumps the
+# version, so `traffic` reads null until the counters are taken again.
 TRAFFIC = {
-    ("long32k", 0, "mla_split_kv_decode_amd 0.2.0 (gfx950)"):
-        {"fetch_kib": 18603.5, "write_kib": 6160.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    ("long32k", 0, "fp32", "mla_split_kv_decode_amd 0.4.0 (gfx950)"):
+        {"fetch_kib": 18589.0, "write_kib": 6240.0, "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
 
@@ -73,6 +73,13 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
+
+
+def partial_kernel_name(wl):
+    """The partial-stage kernel the library picks: one 16-row block (one query token, at
+    most 16 heads) runs the K-split kernel, more row blocks the row-block kernel."""
+    row_blocks = wl.q_len * ((wl.num_heads + 15) // 16)
+    return "mla_partial_ks_kernel" if row_blocks == 1 else "mla_partial_kernel"
 
 
 def describe(wl, splits):
@@ -213,7 +220,7 @@ def main():
     part_gbs = kv_b / (ms_part * 1e-3) / 1e9
     flops = wk.attention_flops(wl.seq_lens, wl.q_len, wl.num_heads, wl.causal)
     traffic = None
-    tr = TRAFFIC.get((wl.name, splits, mb.version()))
+    tr = TRAFFIC.get((wl.name, splits, args.partial, mb.version()))
     if tr:
         traffic = int(1024 * (tr["fetch_kib"] * tr["fetch_factor"] + tr["write_kib"] * tr["write_factor"]))
     res = {
@@ -244,7 +251,7 @@ def main():
             "unit": "GB/s",
             "frac": round(part_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "mla_partial_kernel",
+            "kernel": partial_kernel_name(wl),
             "kernel_us": round(ms_part * 1e3, 3),
             "bytes_per_launch": kv_b,
         },

@@ -92,7 +92,7 @@ int wg_per_cu(bool fp8, int row_blocks) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.3.0 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.4.0 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
