@@ -75,13 +75,6 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
-def partial_kernel_name(wl):
-    """The partial-stage kernel the library picks: one 16-row block (one query token, at
-    most 16 heads) runs the K-split kernel, more row blocks the row-block kernel."""
-    row_blocks = wl.q_len * ((wl.num_heads + 15) // 16)
-    return "mla_partial_ks_kernel" if row_blocks == 1 else "mla_partial_kernel"
-
-
 def describe(wl, splits):
     return (f"{wl.name}: batch {wl.batch}, {wl.num_heads} heads (padded to "
             f"{-(-wl.num_heads // 16) * 16} MFMA rows), {wl.q_len} query token(s), "
@@ -251,7 +244,7 @@ def main():
             "unit": "GB/s",
             "frac": round(part_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": partial_kernel_name(wl),
+            "kernel": "mla_partial_kernel",
             "kernel_us": round(ms_part * 1e3, 3),
             "bytes_per_launch": kv_b,
         },
@@ -259,7 +252,7 @@ def main():
             "full_ms_repeats": [round(x, 6) for x in full_ms],
             "partial_ms_repeats": [round(x, 6) for x in part_ms],
             "merge_and_gap_us": round((ms - ms_part) * 1e3, 3),
-            "units": plan.num_units, "parts": plan.num_parts,
+            "units": plan.num_units, "row_groups": plan.row_groups, "parts": plan.num_parts,
             "mfma_tflops": round(flops / (ms_part * 1e-3) / 1e12, 3),
             "mfma_frac_bf16": round(flops / (ms_part * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
             "io_bytes": wk.io_bytes(wl.seq_lens, wl.q_len, wl.num_heads, wl.kv_format),

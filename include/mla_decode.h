@@ -109,7 +109,7 @@ typedef struct {
  *   q_len         query tokens per request, T >= 1 (T > 1: multi-token verification)
  *   num_heads     real query heads H >= 1; rows are padded to a multiple of 16 inside
  *                 the kernel (padding rows are never loaded or written).  Limit:
- *                 q_len * ceil(H/16) <= 8.
+ *                 q_len * ceil(H/16) <= 64.
  *   softmax_scale scale applied to q.k (e.g. 1/sqrt(192)), finite and > 0
  *   causal        1: token t sees positions 0 .. L-T+t; 0: every token sees all L
  *   num_splits    history partitions per request: 0 = automatic (pages balanced over
@@ -153,9 +153,13 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
                            int32_t page_size, int32_t kv_dtype, int32_t num_cus,
                            mla_plan** plan, size_t* workspace_bytes);
 void mla_plan_destroy(mla_plan* plan);
-/* Workgroups one partial-attention launch uses, and partial slots in the workspace. */
+/* Work units of the partial stage (history ranges; each unit's pieces are the
+ * entries of mla_plan_get_work with that unit index), and partial slots in the workspace. */
 int32_t mla_plan_num_units(const mla_plan* plan);
 int32_t mla_plan_num_parts(const mla_plan* plan);
+/* Workgroups per work unit: the 16-row blocks of the problem (q_len * ceil(num_heads/16))
+ * are dealt to that many workgroups, two per workgroup when their count is even. */
+int32_t mla_plan_row_groups(const mla_plan* plan);
 /*
  * Host copy of the work list, for inspection: 5 int32 per piece
  * (workgroup, request, first page, end page (exclusive), partial slot), in workgroup

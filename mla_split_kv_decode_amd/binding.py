@@ -65,6 +65,7 @@ def _signatures():
         "mla_plan_destroy": (None, [P]),
         "mla_plan_num_units": (c.c_int32, [P]),
         "mla_plan_num_parts": (c.c_int32, [P]),
+        "mla_plan_row_groups": (c.c_int32, [P]),
         "mla_plan_get_work": (c.c_int32, [P, P, c.c_int32]),
         "mla_decode_splitkv": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_size_t, P, c.c_int32,
                                          P, P]),
@@ -167,6 +168,10 @@ class Plan:
     @property
     def num_parts(self):
         return load().mla_plan_num_parts(self._h)
+
+    @property
+    def row_groups(self):
+        return load().mla_plan_row_groups(self._h)
 
     def work(self):
         """Work list as int32 [n][5]: (workgroup, request, first page, end page, slot)."""

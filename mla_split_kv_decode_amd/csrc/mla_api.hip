@@ -18,7 +18,7 @@ namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
                         hipStream_t stream);
-size_t partial_lds_size(bool fp8, int row_blocks);
+size_t partial_lds_size(bool fp8, int rbw);
 }  // namespace mla
 
 using namespace mla;
@@ -30,9 +30,11 @@ struct mla_plan {
   int32_t num_cus;
   int32_t head_groups;
   int32_t row_blocks;
+  int32_t rbw;           // row blocks per workgroup
+  int32_t row_groups;    // workgroups per unit
   int32_t rows;          // q_len * num_heads, real rows
   int32_t mode;          // SplitMode
-  int32_t num_wg;        // workgroups of the partial stage
+  int32_t num_wg;        // work units of the partial stage
   int32_t num_splits;    // S (SPLIT_FIXED)
   int32_t num_slots;     // partial answers the workspace holds
   int32_t part_bf16;     // partial O element type
@@ -81,8 +83,8 @@ void fill_plan_args(const mla_plan& pl, PlanArgs* a) {
 }
 
 // Workgroups per compute unit the partial stage can keep resident (LDS bound).
-int wg_per_cu(bool fp8, int row_blocks) {
-  const size_t lds = partial_lds_size(fp8, row_blocks);
+int wg_per_cu(bool fp8, int rbw) {
+  const size_t lds = partial_lds_size(fp8, rbw);
   const size_t cu_lds = 160 * 1024;
   int n = (int)(cu_lds / ((lds + 1279) / 1280 * 1280));
   return n < 1 ? 1 : (n > 2 ? 2 : n);
@@ -92,7 +94,7 @@ int wg_per_cu(bool fp8, int row_blocks) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.4.0 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.5.0 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -182,6 +184,10 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   pl->num_cus = num_cus;
   pl->head_groups = (int32_t)head_groups;
   pl->row_blocks = (int32_t)row_blocks;
+  // two row blocks per workgroup when they pair up (every K and V^T operand read from LDS
+  // then feeds two MFMAs), else one
+  pl->rbw = row_blocks % 2 == 0 ? 2 : 1;
+  pl->row_groups = (int32_t)row_blocks / pl->rbw;
   pl->rows = s.q_len * s.num_heads;
   pl->total_pages = total_pages;
   pl->max_req_pages = max_req_pages;
@@ -194,15 +200,26 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
     wg = (int64_t)s.batch * s.num_splits;
     slots = wg;
   } else {
-    // Balanced: fill every compute unit (resident workgroups), never more workgroups
-    // than pages.
+    // Balanced: fill every compute unit (resident workgroups, row_groups per unit), never
+    // more units than pages.
     pl->mode = SPLIT_BALANCED;
     pl->num_splits = 0;
-    const int64_t target = (int64_t)num_cus * wg_per_cu(fp8, (int)row_blocks);
+    const int64_t slots_per_cu = (int64_t)num_cus * wg_per_cu(fp8, pl->rbw);
+    const int64_t G = pl->row_groups;
+    int64_t target;
+    if (G == 1) {
+      target = slots_per_cu;
+    } else {
+      // the kernel deals blocks to the eight XCDs by block index and keeps a unit's row
+      // groups on one XCD: whole units per XCD, so that no XCD gets a second round
+      const int64_t per_xcd = slots_per_cu / 8;
+      target = per_xcd >= G ? 8 * (per_xcd / G) : slots_per_cu / G;
+    }
+    if (target < 1) target = 1;
     wg = total_pages < target ? total_pages : target;
     slots = wg + s.batch - 1;
   }
-  if (wg > INT32_MAX / 2 || slots > INT32_MAX / 2) {
+  if (wg > INT32_MAX / 2 || slots > INT32_MAX / 2 || partial_grid(wg, pl->row_groups) > INT32_MAX / 2) {
     delete pl;
     return fail(MLA_ERR_UNSUPPORTED, "too many workgroups");
   }
@@ -224,6 +241,8 @@ void mla_plan_destroy(mla_plan* plan) { delete plan; }
 int32_t mla_plan_num_units(const mla_plan* plan) { return plan ? plan->num_wg : -1; }
 
 int32_t mla_plan_num_parts(const mla_plan* plan) { return plan ? plan->num_slots : -1; }
+
+int32_t mla_plan_row_groups(const mla_plan* plan) { return plan ? plan->row_groups : -1; }
 
 int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity) {
   if (!plan || capacity < 0 || (capacity > 0 && !out)) return -1;
@@ -316,6 +335,8 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   pp.q_len = s.q_len;
   pp.num_heads = s.num_heads;
   pp.head_groups = plan->head_groups;
+  pp.rbw = plan->rbw;
+  pp.row_groups = plan->row_groups;
   pp.rows = plan->rows;
   pp.causal = s.causal;
   pp.mode = plan->mode;

@@ -9,15 +9,18 @@
 // to the block-table row length), and the requests' pages are laid end to end on a
 // global axis g = pre_r + local page, pre_r = sum_{s<r} pages_s, P = sum_r pages_r.
 //
-//  * SPLIT_BALANCED (num_splits = 0): W workgroups, W <= P.  Workgroup w takes global
-//    pages [floor(w P / W), floor((w+1) P / W)), which may span several requests.  Each
-//    (workgroup, request) overlap is one piece with its own partial answer, stored in
-//    slot w + r.  Along the global axis both w and r only grow, so no two pieces share
-//    a slot, and the pieces of request r occupy the contiguous slot range
+//  * SPLIT_BALANCED (num_splits = 0): W work units, W <= P.  Unit w takes global pages
+//    [floor(w P / W), floor((w+1) P / W)), which may span several requests.  Each
+//    (unit, request) overlap is one piece with its own partial answer, stored in slot
+//    w + r.  Along the global axis both w and r only grow, so no two pieces share a
+//    slot, and the pieces of request r occupy the contiguous slot range
 //    [wg_of(pre_r) + r, wg_of(pre_r + pages_r - 1) + r].  Slots: W + B - 1.
-//  * SPLIT_FIXED (num_splits = S >= 1): W = B * S workgroups; workgroup w = r S + s takes
-//    the request's local pages [floor(s pages_r / S), floor((s+1) pages_r / S)) and slot
-//    w.  A piece may be empty (pages_r < S); it then stores LSE = -inf and O = 0.
+//  * SPLIT_FIXED (num_splits = S >= 1): W = B * S units; unit w = r S + s takes the
+//    request's local pages [floor(s pages_r / S), floor((s+1) pages_r / S)) and slot w.
+//    A piece may be empty (pages_r < S); it then stores LSE = -inf and O = 0.
+//
+// A unit runs as row_groups workgroups, each computing the unit's pieces for its own
+// row blocks (16 query rows each), i.e. its own rows of every slot.
 //
 // Both the host planner (for inspection and sizing) and the device kernels evaluate the
 // same closed forms below, from seq_lens; the device never needs an uploaded work list.
@@ -37,7 +40,7 @@ constexpr int kPage = 64;          // positions per page
 constexpr int kDLatent = 576;      // latent width (key = all columns)
 constexpr int kDV = 512;           // value width (first columns of the latent)
 constexpr int kRowsPerBlock = 16;  // MFMA rows: heads are padded to a multiple of 16
-constexpr int kMaxRowBlocks = 8;   // q_len * ceil(heads / 16) limit of one workgroup
+constexpr int kMaxRowBlocks = 64;  // q_len * ceil(heads / 16) limit of one call
 
 enum SplitMode : int32_t { SPLIT_BALANCED = 0, SPLIT_FIXED = 1 };
 
@@ -71,10 +74,10 @@ MLA_HD int64_t div_floor_fast(int64_t x, int64_t y) {
   return div_floor(x, y);
 }
 
-// First global page of workgroup w under SPLIT_BALANCED.
+// First global page of unit w under SPLIT_BALANCED.
 MLA_HD int64_t balanced_start(int64_t w, int64_t P, int64_t W) { return div_floor_fast(w * P, W); }
 
-// Workgroup holding global page g under SPLIT_BALANCED (largest w with start(w) <= g).
+// Unit holding global page g under SPLIT_BALANCED (largest w with start(w) <= g).
 MLA_HD int64_t balanced_wg_of(int64_t g, int64_t P, int64_t W) { return div_floor_fast((g + 1) * W - 1, P); }
 
 MLA_HD int32_t fixed_page_begin(int32_t s, int32_t pages, int32_t S) {
@@ -92,6 +95,11 @@ struct PlanArgs {
   int32_t pre[kArgBatch + 1];   // pre[r] = sum_{s<r} ceil(len[s] / kPage)
 };
 
+// Blocks of a partial-stage launch: W units times the row groups, rounded up to whole
+// groups of eight units when there are several row groups (block b serves unit
+// 8 (b / 8 / G) + b % 8, row group (b / 8) % G; see the kernel).
+MLA_HD int64_t partial_grid(int64_t W, int32_t G) { return G == 1 ? W : (W + 7) / 8 * 8 * G; }
+
 // Launch parameters of the partial-attention kernel.
 struct PartialParams {
   const uint16_t* q;          // bf16 [B][T][H][576]
@@ -103,9 +111,11 @@ struct PartialParams {
   int64_t num_pages;
   int32_t max_pages;
   int32_t batch, q_len, num_heads, head_groups, rows;  // rows = T * H
+  int32_t rbw;        // row blocks per workgroup (1 or 2)
+  int32_t row_groups; // workgroups per work unit: q_len * head_groups / rbw
   int32_t causal;
   int32_t mode;       // SplitMode
-  int32_t num_wg;     // W
+  int32_t num_wg;     // W work units
   int32_t num_splits; // S (SPLIT_FIXED)
   int32_t num_slots;  // slot stride of the partial layout
   int32_t part_bf16;  // partial O element type: 1 bf16, 0 fp32

@@ -1,37 +1,39 @@
 // gfx950 kernels of absorbed-MLA split-KV decode.
 //
-// Stage 1, mla_partial_kernel: one workgroup per piece list (see mla_internal.h).  For
-// each piece (request, page range) it streams the latent pages into LDS and computes,
-// for every query row of the request, the softmax-attention partial answer over the
-// piece: O_p (normalised, fp32) and LSE_p.  Kimi K3 on MI355X, section 4 "MLA": the
-// history is split into partitions handled by separate workgroups; section 1 "Cache",
-// DCP8 paragraph: a partial answer carries its normalisation so pieces can be merged.
+// Stage 1, mla_partial_kernel: work unit w (see mla_internal.h) runs as row_groups
+// workgroups, each owning one or two row blocks of 16 query rows.  For each piece of the
+// unit (request, page range) a workgroup streams the latent pages into LDS and computes,
+// for its rows, the softmax-attention partial answer over the piece: O_p (normalised)
+// and LSE_p.  Kimi K3 on MI355X, section 4 "MLA": the history is split into partitions
+// handled by separate workgroups; section 1 "Cache", DCP8 paragraph: a partial answer
+// carries its normalisation so pieces can be merged.
 //
 // Stage 2, mla_merge_kernel: the LSE-weighted merge of the partial answers of each row.
 //
 // Data movement.  A page (64 positions x 576 latent values) is copied from HBM straight
-// into an LDS tile with global_load_lds_dwordx4 (no staging registers); two tiles per
-// workgroup, so the next page streams in while the current one is consumed, and a piece
-// of two pages has its whole history in flight at once.  Within a tile each 16-byte
-// chunk of a row sits at an XOR-swizzled column so that the MFMA operand reads below hit
-// distinct LDS banks; the DMA fills the tile in contiguous 1 KiB blocks and each lane
-// fetches the global chunk that belongs at its slot.
+// into an LDS tile with global_load_lds_dwordx4 (no staging registers); two bf16 tiles
+// (four FP8 tiles) per workgroup, so the next pages stream in while the current one is
+// consumed, and a piece of two pages has its whole history in flight at once.  Within a
+// tile each 16-byte chunk of a row sits at an XOR-swizzled column so that the MFMA
+// operand reads below hit distinct LDS banks; the copy fills the tile in contiguous 1 KiB
+// blocks and each lane fetches the global chunk that belongs at its slot.
 //
 // Matrix layout (all on the 16x16 MFMA grid, wave64):
 //  * rows   : 16 query rows = 16 heads of one query token ("row block"); heads past the
-//             real count are zero rows (section 4: padding heads leaves real heads
-//             unchanged) that are never loaded or written.
+//             real count repeat the last real head (section 4: padding heads leaves real
+//             heads unchanged) and are never written.
 //  * QK^T   : S^T[pos][row] = sum_k K[pos][k] Q[row][k] with v_mfma_f32_16x16x32_bf16,
 //             A = 16 positions x 32 latent columns read from the LDS tile, B = the row
 //             block's queries, kept in registers for the whole piece.
 //  * PV     : O^T[col][row] += sum_pos V^T[col][pos] P^T[pos][row].  The S^T accumulator
 //             layout (lane = row, 4 consecutive positions per lane) is already the B
-//             layout of the next MFMA, so P never leaves registers (or, when several
-//             waves share a row block, takes one small LDS exchange).  V^T is read from
-//             the same LDS tile with the gfx950 transposing LDS reads (ds_read_b64_tr_b16
-//             for bf16, ds_read_b64_tr_b8 for FP8), so each latent byte leaves HBM once.
-//  * softmax: online, in log2 units; the row max is a 2-step cross-lane reduction and,
-//             across waves of one row block, an LDS exchange.
+//             layout of the next MFMA; P takes one small LDS exchange between the waves
+//             that computed it and the waves that own the output columns.  V^T is read
+//             from the same LDS tile with the gfx950 transposing LDS reads
+//             (ds_read_b64_tr_b16 for bf16, ds_read_b64_tr_b8 for FP8), so each latent
+//             byte leaves HBM once per workgroup.
+//  * softmax: online, in log2 units, with an exact running max; the row max is a
+//             cross-lane reduction (row swaps) and an LDS exchange between the waves.
 #include <hip/hip_runtime.h>
 
 #include "mla_internal.h"
@@ -82,46 +84,50 @@ __device__ __forceinline__ void barrier_lds() {
 // compiler cannot tell these buffers from the page tiles being filled by copies still in
 // flight and would otherwise wait for all of them first.  Each call completes its reads
 // (lgkmcnt(0)) before returning.  `off` is the LDS byte address.
+// Only for addresses the compiler can fold (a member of the workgroup's __shared__
+// object at a constant offset): a run-time generic-to-LDS cast carries a null check on the
+// shared aperture, which the gfx950 code generator can emit as an illegal instruction.
+// Everything else takes integer LDS offsets from such a base.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 template <int G>
-__device__ __forceinline__ float lds_max_of(const float* p, float init) {
-  // max of p[0], p[16], ..., p[16 (G-1)] and init
+__device__ __forceinline__ float lds_max_of(uint32_t off, float init) {
+  // max of the floats at LDS byte offsets off, off + 64, ..., off + 64 (G-1), and init
   float v[4];
   if constexpr (G == 4) {
     asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:64\n\t"
                  "ds_read_b32 %2, %4 offset:128\n\tds_read_b32 %3, %4 offset:192\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]) : "v"(lds_addr(p)));
+                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]) : "v"(off));
     return fmaxf(fmaxf(fmaxf(init, v[0]), fmaxf(v[1], v[2])), v[3]);
   } else {
     static_assert(G == 2, "exchange width");
     asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:64\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]) : "v"(lds_addr(p)));
+                 : "=v"(v[0]), "=v"(v[1]) : "v"(off));
     return fmaxf(fmaxf(init, v[0]), v[1]);
   }
 }
 template <int G>
-__device__ __forceinline__ float lds_sum_of(const float* p) {
+__device__ __forceinline__ float lds_sum_of(uint32_t off) {
   float v[4];
   if constexpr (G == 4) {
     asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:64\n\t"
                  "ds_read_b32 %2, %4 offset:128\n\tds_read_b32 %3, %4 offset:192\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]) : "v"(lds_addr(p)));
+                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]) : "v"(off));
     return ((v[0] + v[1]) + v[2]) + v[3];
   } else {
     static_assert(G == 2, "exchange width");
     asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:64\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]) : "v"(lds_addr(p)));
+                 : "=v"(v[0]), "=v"(v[1]) : "v"(off));
     return v[0] + v[1];
   }
 }
 // two 16-byte reads 1 KiB apart (the two 32-position P^T chunks of a row block)
-__device__ __forceinline__ void lds_read_pair_b128(const void* p, i32x4& a, i32x4& b) {
+__device__ __forceinline__ void lds_read_pair_b128(uint32_t off, i32x4& a, i32x4& b) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(a), "=v"(b) : "v"(lds_addr(p)));
+               : "=v"(a), "=v"(b) : "v"(off));
 }
 
 // A load of one int32 through the vector memory path.  Uniform loads would otherwise be
@@ -132,6 +138,23 @@ __device__ __forceinline__ int32_t vector_load_i32(const int32_t* p) {
   int32_t z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
   return p[z];
+}
+
+// Max and sum of a value over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane
+// rows of a wave): the gfx950 row-swap instructions exchange whole rows between two
+// registers, so the larger (or the sum) of the two results combines each lane with its
+// partner without an LDS round trip.
+__device__ __forceinline__ float max_over_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Eight FP8 E4M3FN codes (little-endian bytes of `raw`) -> eight bf16, exactly.
@@ -253,9 +276,8 @@ struct PageCopy {
   // The copies are issued as inline assembly so that the compiler neither delays LDS
   // reads of the other tiles behind them nor counts them: every wait on them is explicit
   // (wait_vmcnt), and they complete in issue order with the other vector-memory ops.
-  __device__ __forceinline__ void operator()(unsigned char* tile, const unsigned char* src,
+  __device__ __forceinline__ void operator()(uint32_t base, const unsigned char* src,
                                              int valid_rows) const {
-    const uint32_t base = lds_addr(tile);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       int off = src_off[j];
@@ -270,11 +292,12 @@ struct PageCopy {
   }
 };
 
-// Copy the queries of a workgroup's RB row blocks (request r) into an LDS staging area of
-// RB x 16 rows of 576 bf16, laid out like a bf16 page tile (same chunk swizzle), so one
-// HBM read serves every wave that shares a row block.  Row i of row block rb is head
-// 16 hg + i of token t (rb = t * head_groups + hg); a padding head repeats the last real
-// head (its results are discarded).  Same operation-count rule as PageCopy.
+// Copy the queries of a workgroup's RB row blocks rb0 .. rb0 + RB - 1 (request r) into an
+// LDS staging area of RB x 16 rows of 576 bf16, laid out like a bf16 page tile (same chunk
+// swizzle), so one HBM read serves every wave that shares a row block.  Row i of row
+// block rb is head 16 hg + i of token t (rb = t * head_groups + hg); a padding head
+// repeats the last real head (its results are discarded).  Same operation-count rule as
+// PageCopy.
 template <int NW, int RB>
 struct QueryCopy {
   using TG = TileGeom<false>;
@@ -282,16 +305,16 @@ struct QueryCopy {
   static constexpr int kPer = (kBlocks + NW - 1) / NW;
   int wave, lane;
   __device__ __forceinline__ QueryCopy(int wave_, int lane_) : wave(wave_), lane(lane_) {}
-  __device__ __forceinline__ void operator()(unsigned char* stage, const uint16_t* q_req,
-                                             int num_heads, int head_groups) const {
-    const uint32_t base = lds_addr(stage);
+  __device__ __forceinline__ void operator()(uint32_t base, const uint16_t* q_req,
+                                             int num_heads, int head_groups, int rb0) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       int k = wave + NW * j;
       k = k < kBlocks ? k : kBlocks - 1;
       const int s = k * 64 + lane;
       const int row = s / TG::kChunksPerRow, cs = s - row * TG::kChunksPerRow;
-      const int rb = row / kRowsPerBlock, i = row - rb * kRowsPerBlock;
+      const int lrb = row / kRowsPerBlock, i = row - lrb * kRowsPerBlock;
+      const int rb = rb0 + lrb;
       const int t = rb / head_groups, hg = rb - t * head_groups;
       const int head = min(hg * kRowsPerBlock + i, num_heads - 1);
       const int off = (t * num_heads + head) * TG::kRowBytes + TG::swz(row, cs) * 16;
@@ -314,58 +337,30 @@ __device__ __forceinline__ void wait_pages(int n) {
   else wait_vmcnt<0>();
 }
 
-// Shape of the partial-attention workgroup.  RB row blocks of 16 query rows; G waves
-// share a row block (they split its positions for QK^T and its output columns for PV);
-// NG groups of RB * G waves run in lockstep on consecutive pages, each group on its own
-// page, and combine their answers at the end of a piece.
-template <bool FP8, int G_, int RB_, int NG_>
-struct PartialCfg {
-  static constexpr int G = G_, RB = RB_, NG = NG_;
-  using TG = TileGeom<FP8>;
-  static constexpr int WPG = RB * G;                // waves per group
-  static constexpr int NW = NG * WPG;               // waves per workgroup
-  static constexpr int NST = 4 / G;                 // 16-position sub-tiles of a page per wave
-  static constexpr int CT = 32 / G;                 // 16-column output tiles per wave
-  static constexpr int kTiles = FP8 ? 4 : 2;        // page tiles in LDS (147,456 bytes)
-  static constexpr int kSIF = kTiles / NG;          // steps (NG pages each) in flight
-  static constexpr int kPer = PageCopy<FP8, NW>::kPer;
-  // queries go through LDS when several waves need the same row block
-  static constexpr bool kQLds = G > 1 || NG > 1;
-  static constexpr int kQPer = kQLds ? QueryCopy<NW, RB>::kPer : 0;
-  static constexpr int kQTiles =
-      kQLds ? (QueryCopy<NW, RB>::kBlocks * 1024 + TG::kPageBytes - 1) / TG::kPageBytes : 0;
-  static constexpr int kXBytes = G > 1 ? NG * RB * 2 * 64 * 16 : 16;  // P exchange
-  static_assert(G == 1 || G == 2 || G == 4, "waves per row block");
-  static_assert(RB >= 1 && RB <= kMaxRowBlocks && NW <= 16, "workgroup shape");
-  static_assert(kTiles % NG == 0 && kQTiles < kTiles, "tile plan");
-  static_assert(kPer * kTiles + kQPer <= 63, "outstanding operations exceed vmcnt");
-  static_assert(NG == 1 || G > 1, "the group combine relies on the denominator barrier");
-};
-
 // Every scalar argument a partial-stage prologue needs, fetched in one batch: the compiler
 // would otherwise load some fields lazily inside branches, one memory round trip each,
 // before the first page copy can be issued.
 struct HotArgs {
-  int heads, hgroups, mode, nwg, nsplits, plan_n, len0, maxp, batch, qlen, causal, nslots, pbf16;
+  int heads, hgroups, rgroups, mode, nwg, nsplits, plan_n, len0, maxp, batch, qlen, causal, nslots, pbf16;
   int64_t total, npages;
   float sscale, vscale;
   __device__ __forceinline__ explicit HotArgs(const PartialParams& p)
-      : heads(p.num_heads), hgroups(p.head_groups), mode(p.mode), nwg(p.num_wg),
+      : heads(p.num_heads), hgroups(p.head_groups), rgroups(p.row_groups), mode(p.mode), nwg(p.num_wg),
         nsplits(p.num_splits), plan_n(p.plan.n), len0(p.plan.len[0]), maxp(p.max_pages),
         batch(p.batch), qlen(p.q_len), causal(p.causal), nslots(p.num_slots), pbf16(p.part_bf16),
         total(p.total_pages), npages(p.num_pages), sscale(p.score_scale), vscale(p.v_scale) {
-    asm volatile("" ::"s"(heads), "s"(hgroups), "s"(mode), "s"(nwg), "s"(nsplits), "s"(plan_n),
+    asm volatile("" ::"s"(heads), "s"(hgroups), "s"(rgroups), "s"(mode), "s"(nwg), "s"(nsplits), "s"(plan_n),
                  "s"(len0), "s"(maxp), "s"(batch), "s"(qlen), "s"(causal), "s"(nslots), "s"(pbf16),
                  "s"(total), "s"(npages), "s"(sscale), "s"(vscale));
   }
 };
 
-// The pieces of workgroup blockIdx.x (mla_internal.h): run(r, first page, end page, slot, L)
-// for each, from the plan's lengths in the arguments when present, else from seq_lens.
+// The pieces of work unit w (mla_internal.h): run(r, first page, end page, slot, L) for
+// each, from the plan's lengths in the arguments when present, else from seq_lens.
 template <class F>
 __device__ __forceinline__ void for_each_piece(const PartialParams& p, const HotArgs& a,
-                                               const int32_t* __restrict__ seq_lens, F&& run_piece) {
-  const int64_t w = blockIdx.x;
+                                               const int32_t* __restrict__ seq_lens, int64_t w,
+                                               F&& run_piece) {
   const bool use_plan = a.plan_n > 0;
   if (a.mode == SPLIT_FIXED) {
     const int S = a.nsplits;
@@ -417,425 +412,106 @@ __device__ __forceinline__ void store_partial(void* part_o, bool bf16, int64_t o
     *(f32x4*)((float*)part_o + idx) = v;
 }
 
-template <class C>
-struct PartialSmem {
-  using TG = typename C::TG;
-  __attribute__((aligned(1024))) unsigned char tiles[C::kTiles * TG::kPageBytes];
-  __attribute__((aligned(16))) unsigned char pbuf[C::kXBytes];  // P of a step
-  float red[C::NW * 16];   // row maxima of a step
-  float red2[C::NW * 16];  // row denominators of the epilogue
-  float xch[C::NG * C::RB * 16 * 2];
-};
-
-// Stage 1 for workgroup blockIdx.x: every piece it owns, partial answers to the workspace.
-// The device pointers are separate __restrict__ arguments: read-only, never aliased by
-// the output stores, so uniform reads (lengths, page ids) become scalar loads.
-template <bool FP8, class C>
-__device__ __forceinline__ void partial_phase(
-    const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    void* __restrict__ part_o, float* __restrict__ part_lse, PartialSmem<C>& sm) {
-  using TG = TileGeom<FP8>;
-  using Copy = PageCopy<FP8, C::NW>;
-  constexpr int G = C::G, RB = C::RB, NG = C::NG, WPG = C::WPG, NST = C::NST, CT = C::CT;
-  constexpr int kTiles = C::kTiles, kSIF = C::kSIF, kPer = C::kPer;
-  constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
-
-  const HotArgs args(p);
-  const int a_heads = args.heads, a_hgroups = args.hgroups, a_maxp = args.maxp;
-  const int a_qlen = args.qlen, a_causal = args.causal, a_nslots = args.nslots, a_pbf16 = args.pbf16;
-  const int64_t a_npages = args.npages;
-  const float a_sscale = args.sscale, a_vscale = args.vscale;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 15, lgrp = lane >> 4;
-  const int grp = wave / WPG, wig = wave - grp * WPG;  // group, wave in group
-  const int rb = wig / G, g = wig - (wig / G) * G;
-  const int t = rb / a_hgroups, hg = rb - t * a_hgroups;
-  const int head = hg * kRowsPerBlock + lrow;
-  const bool head_ok = head < a_heads;
-  const Copy copy(wave, lane);
-  const OperandAddr<FP8> addr(lrow, lgrp, g * CT);
-  unsigned char* const tiles = sm.tiles;
-  unsigned char* const pbuf = sm.pbuf;
-  float* const red = sm.red;
-
-  // One piece: request r of length L, local pages [pb, pe), partial slot `slot`.  With
-  // the plan's lengths in the arguments no device length is read here (a pending load of
-  // it would be waited for at the first page copy's inline assembly): the merge stage
-  // compares the device lengths with the plan's.
-  auto run_piece = [&](int r, int pb, int pe, int64_t slot, int L) {
-    const int limit = a_causal ? L - a_qlen + t + 1 : L;  // visible: position < limit
-    const int32_t* trow = block_table + (int64_t)r * a_maxp;
-    const int n = pe - pb;                   // pages of the piece
-    const int nsteps = (n + NG - 1) / NG;    // step s: page s * NG + group
-    bool bad = false;
-
-    // A page id outside the pool is never dereferenced: the copy reads page 0 instead
-    // (keeping the per-wave operation count) and the piece's result becomes NaN.
-    auto issue = [&](int s, int gi) {
-      const int i = s * NG + gi;
-      if (i >= n) return;
-      const int lp = pb + i;
-      int32_t id = trow[lp];
-      if ((uint64_t)(int64_t)id >= (uint64_t)a_npages) {
-        bad = true;
-        id = 0;
-      }
-      const int valid_rows = min(kPage, L - lp * kPage);
-      copy(tiles + ((s % kSIF) * NG + gi) * TG::kPageBytes, pool + (int64_t)id * TG::kPageBytes,
-           valid_rows);
-    };
-
-    // ---- queries and the first pages
-    i32x4 qf[kDLatent / 32];
-    const uint16_t* q_req = q_ptr + (int64_t)r * a_qlen * a_heads * kDLatent;
-    if constexpr (C::kQLds) {
-      unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
-      QueryCopy<C::NW, RB>(wave, lane)(stage, q_req, a_heads, a_hgroups);
-      int early = 0;
-#pragma unroll
-      for (int ti = 0; ti < kEarlyTiles; ++ti) {
-        issue(ti / NG, ti % NG);
-        early += (ti < n) ? 1 : 0;
-      }
-      wait_pages<kPer, kEarlyTiles>(early);  // the query copies are older: all landed
-      barrier_lds();
-      const OperandAddr<false> qa(lrow, lgrp, 0);
-      const unsigned char* qb = stage + rb * kRowsPerBlock * TileGeom<false>::kRowBytes;
-#pragma unroll
-      for (int kk = 0; kk < kDLatent / 32; ++kk)
-        qf[kk] = *(const i32x4*)(qb + qa.kbase[kk & 1] + OperandAddr<false>::kstep(kk));
-      barrier_lds();  // the staging tiles are free again
-#pragma unroll
-      for (int ti = kEarlyTiles; ti < kTiles; ++ti) issue(ti / NG, ti % NG);
-    } else {
-      // One wave per row block: the page copies go out first, then the queries as
-      // ordinary loads.  The compiler waits for those at the next inline assembly (the
-      // first step's wait), so that step also waits for the prefetched pages; later steps
-      // are unaffected.  A padding row repeats the last real head.
-#pragma unroll
-      for (int ti = 0; ti < kTiles; ++ti) issue(ti / NG, ti % NG);
-      const int hq = head_ok ? head : a_heads - 1;
-      const uint16_t* qrow = q_req + ((int64_t)t * a_heads + hq) * kDLatent + lgrp * 8;
-#pragma unroll
-      for (int kk = 0; kk < kDLatent / 32; ++kk) qf[kk] = *(const i32x4*)(qrow + kk * 32);
-    }
-
-    float m = kNegInf;   // running max of this lane's row (log2 units)
-    float lsum = 0.f;    // this lane's share of the running denominator
-    f32x4 acc[CT];
-#pragma unroll
-    for (int i = 0; i < CT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = 0; s < nsteps; ++s) {
-      // pages of steps s+1 .. s+kSIF-1 were issued after this step's: let them fly
-      wait_pages<kPer, (kSIF - 1) * NG>(min(n, (s + kSIF) * NG) - min(n, (s + 1) * NG));
-      barrier_lds();  // every wave's copies of this step have landed
-      const int i = s * NG + grp;
-      const bool has = i < n;  // uniform in the group
-      const unsigned char* tile = tiles + ((s % kSIF) * NG + grp) * TG::kPageBytes;
-      const int lp = pb + i;
-
-      // ---- S^T = K Q^T for this wave's sub-tiles, scale, mask, tile max.  When registers
-      // allow (a wave with at most 8 output column tiles), the V^T operands of the first
-      // PV chunk are read right after the QK^T MFMAs are issued: they do not depend on the
-      // softmax, so those transposing LDS reads run under the MFMAs and the exchanges.
-      constexpr int kEarly = CT <= 8 ? 1 : 0;  // PV chunks whose operands are read early
-      f32x4 sv[NST];
-      bf16x8 va[2][CT];
-      auto read_v = [&](int c) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const unsigned char* va0 =
-              tile + c * 32 * TG::kRowBytes + addr.vbase[ct & 3] + OperandAddr<FP8>::vstep(ct);
-          if constexpr (FP8) {
-            va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
-          } else {
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
-            const bf16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
-            va[c][ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-        }
-      };
-      float mx = kNegInf;
-      if (has) {
-#pragma unroll
-        for (int u = 0; u < NST; ++u) {
-          const unsigned char* kt = tile + (g * NST + u) * 16 * TG::kRowBytes;
-          bf16x8 kf[kDLatent / 32];
-#pragma unroll
-          for (int kk = 0; kk < kDLatent / 32; ++kk) {
-            const unsigned char* ka = kt + addr.kbase[kk & 1] + OperandAddr<FP8>::kstep(kk);
-            if constexpr (FP8) kf[kk] = fp8x8_to_bf16x8(*(const i32x2*)ka);
-            else kf[kk] = *(const bf16x8*)ka;
-          }
-          // one accumulation chain in k-step order (dependent MFMAs forward their
-          // accumulator), so that each MFMA consumes the oldest outstanding K read
-          f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < kDLatent / 32; ++kk)
-            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], __builtin_bit_cast(bf16x8, qf[kk]),
-                                                         a0, 0, 0, 0);
-          sv[u] = a0;
-          if constexpr (kEarly > 0) read_v(0);  // kEarly implies one sub-tile per wave
-          if constexpr (!FP8) {
-            // Instruction order of the sub-tile: six K reads ahead, then one MFMA per
-            // read, so LDS latency hides under the MFMAs; the early V^T reads go between
-            // the last six MFMAs.  (Left alone, the scheduler keeps only one or two reads
-            // ahead and each MFMA waits for its operand.)
-            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-            for (int i = 0; i < 12; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            if constexpr (kEarly > 0) {
-              static_assert(NST == 1 && 2 * CT == 16, "early V^T reads: one chunk, 16 reads");
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-              }
-#pragma unroll
-              for (int i = 0; i < 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-              }
-            } else {
-              __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-            }
-          }
-        }
-        const int pos0 = lp * kPage;
-#pragma unroll
-        for (int u = 0; u < NST; ++u) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = pos0 + (g * NST + u) * 16 + lgrp * 4 + e;
-            const float v = j < limit ? sv[u][e] * a_sscale : kNegInf;
-            sv[u][e] = v;
-            mx = fmaxf(mx, v);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < NST; ++u) sv[u] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if constexpr (G > 1) {
-        if (lgrp == 0) red[(grp * WPG + rb * G + g) * 16 + lrow] = mx;
-        barrier_lds();
-        mx = lds_max_of<G>(&red[(grp * WPG + rb * G) * 16 + lrow], mx);
-      }
-
-      // ---- online softmax update
-      const float m_new = fmaxf(m, mx);
-      const float msub = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m - msub);  // m = -inf -> 0
-      m = m_new;
-      float ps = 0.f;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int u = 0; u < NST; ++u) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = exp2_fast(sv[u][e] - msub);
-          sv[u][e] = pv;
-          ps += pv;
-        }
-      }
-      lsum = lsum * alpha + ps;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] *= alpha;
-
-      // ---- P^T as the B operand of the PV MFMA: slots 0-3 = positions 4*lgrp+0..3 of
-      // the chunk's first 16-position sub-tile, slots 4-7 = the same of its second.
-      if constexpr (G == 1) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          pf[c] = bf16x8{(__bf16)sv[2 * c][0], (__bf16)sv[2 * c][1], (__bf16)sv[2 * c][2],
-                         (__bf16)sv[2 * c][3], (__bf16)sv[2 * c + 1][0], (__bf16)sv[2 * c + 1][1],
-                         (__bf16)sv[2 * c + 1][2], (__bf16)sv[2 * c + 1][3]};
-        }
-      } else {
-        unsigned char* pb_rb = pbuf + (grp * RB + rb) * 2 * 64 * 16;
-#pragma unroll
-        for (int u = 0; u < NST; ++u) {
-          const int pt = g * NST + u;
-          bf16x4 v = bf16x4{(__bf16)sv[u][0], (__bf16)sv[u][1], (__bf16)sv[u][2], (__bf16)sv[u][3]};
-          *(bf16x4*)(pb_rb + ((pt >> 1) * 64 + lane) * 16 + (pt & 1) * 8) = v;
-        }
-        barrier_lds();
-        i32x4 p0, p1;
-        lds_read_pair_b128(pb_rb + lane * 16, p0, p1);
-        pf[0] = __builtin_bit_cast(bf16x8, p0);
-        pf[1] = __builtin_bit_cast(bf16x8, p1);
-      }
-
-      // ---- O^T += V^T P^T over the page's two 32-position chunks
-      if (has) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          if (c >= kEarly) read_v(c);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[ct], 0, 0, 0);
-        }
-      }
-
-      // The next copies into this step's tiles wait until every wave is done with them.
-      // Without copies (the last steps) no barrier is needed: the exchange buffers of the
-      // next step are written only after its own first barrier, and the epilogue uses
-      // buffers of its own (the group combine reuses the tiles only after the
-      // denominator barrier, by which every wave has finished its last V^T reads).
-      if ((s + kSIF) * NG < n) {
-        barrier_lds();
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) issue(s + kSIF, gi);
-      }
-    }
-
-    // ---- epilogue: partial answers go to [row][32-column chunk][slot][32] (bf16 or fp32)
-    const int64_t orow = (int64_t)t * a_heads + head;
-    auto store_o = [&](int ct, f32x4 v) {
-      store_partial(part_o, a_pbf16, orow, g * CT * 16 + ct * 16 + lgrp * 4, a_nslots, slot, v);
-    };
-    // the group's full row denominator
-    float ls = lsum;
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    if constexpr (G > 1) {
-      if (lgrp == 0) sm.red2[(grp * WPG + rb * G + g) * 16 + lrow] = ls;
-      barrier_lds();
-      ls = lds_sum_of<G>(&sm.red2[(grp * WPG + rb * G) * 16 + lrow]);
-    }
-    if constexpr (NG == 1) {
-      const bool empty = m == kNegInf;
-      float oscale = empty ? 0.f : a_vscale / ls;
-      float lse = empty ? kNegInf : (m + log2_fast(ls)) * kLn2;
-      if (bad) {
-        oscale = __builtin_nanf("");
-        lse = __builtin_nanf("");
-      }
-      if (head_ok) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) store_o(ct, acc[ct] * oscale);
-        if (g == 0 && lgrp == 0) part_lse[orow * a_nslots + slot] = lse;
-      }
-    } else {
-      // ---- the two groups combine: (m, l) through LDS, then each wave keeps half of its
-      // output columns and receives its partner's (same row block and columns, other
-      // group) copy of that half through the now idle page tiles.
-      static_assert(NG == 2 && CT % 2 == 0, "group combine");
-      constexpr int H2 = CT / 2;
-      float* xm = sm.xch + ((grp * RB + rb) * 16 + lrow) * 2;
-      if (g == 0 && lgrp == 0) {
-        xm[0] = m;
-        xm[1] = ls;
-      }
-      float* xa = (float*)tiles;  // [wave][H2][64 lanes][4]
-#pragma unroll
-      for (int c = 0; c < H2; ++c) {
-        const f32x4 v = grp == 0 ? acc[H2 + c] : acc[c];
-        *(f32x4*)(xa + ((wave * H2 + c) * 64 + lane) * 4) = v;
-      }
-      barrier_lds();
-      const float* xo = sm.xch + (((1 - grp) * RB + rb) * 16 + lrow) * 2;
-      const float m_o = xo[0], l_o = xo[1];
-      const float M = fmaxf(m, m_o);
-      const float Msub = M == kNegInf ? 0.f : M;
-      const float a_s = exp2_fast(m - Msub), a_o = exp2_fast(m_o - Msub);
-      const float Lsum = a_s * ls + a_o * l_o;
-      const bool empty = M == kNegInf;
-      float oscale = empty ? 0.f : a_vscale / Lsum;
-      float lse = empty ? kNegInf : (M + log2_fast(Lsum)) * kLn2;
-      if (bad) {
-        oscale = __builtin_nanf("");
-        lse = __builtin_nanf("");
-      }
-      const int partner = (1 - grp) * WPG + wig;
-      const float* xp = xa + (partner * H2 * 64 + lane) * 4;
-      if (head_ok) {
-        if (grp == 0) {
-#pragma unroll
-          for (int c = 0; c < H2; ++c) {
-            const f32x4 o = *(const f32x4*)(xp + c * 64 * 4);
-            store_o(c, (acc[c] * a_s + o * a_o) * oscale);
-          }
-          if (g == 0 && lgrp == 0) part_lse[orow * a_nslots + slot] = lse;
-        } else {
-#pragma unroll
-          for (int c = 0; c < H2; ++c) {
-            const f32x4 o = *(const f32x4*)(xp + c * 64 * 4);
-            store_o(H2 + c, (acc[H2 + c] * a_s + o * a_o) * oscale);
-          }
-        }
-      }
-    }
-    barrier_lds();  // tiles and exchange buffers are reused by the next piece
-  };
-
-  for_each_piece(p, args, seq_lens, run_piece);
-}
-
-
-// ------------------------------------------------------------------- K-split partial stage
+// ------------------------------------------------------------------- partial stage
 //
-// One row block of 16 query rows (one query token, up to 16 heads), eight waves per
-// workgroup, all on the same page.  In QK^T wave w computes the partial scores of the
-// 16-position sub-tile u = w & 3 over half kh = w >> 2 of the latent (nine of the 18
-// k-steps of 32 columns); the two halves are added through LDS.  In PV wave w produces
-// output columns [64 w, 64 w + 64) over the page's 64 positions.  One softmax state for the
-// whole workgroup, pages double-buffered (FP8: four in flight), and a page is processed as
-// soon as it has landed, so once the stream ends only the last page's work remains.
-template <bool FP8>
+// A workgroup of eight waves owns RBW row blocks of 16 query rows (RBW = 1 or 2) and the
+// pieces of one work unit; all eight waves work on the same page.  In QK^T wave w
+// computes the partial scores of the 16-position sub-tile u = w & 3 over half kh = w >> 2
+// of the latent (nine of the 18 k-steps of 32 columns) for each of its row blocks: every K
+// operand read from LDS serves all of them.  The two halves are added through LDS.  In
+// PV wave w produces output columns [64 w, 64 w + 64) of every row block over the page's
+// 64 positions, every V^T operand read serving all row blocks.  One softmax state per row
+// block for the whole workgroup, pages double-buffered (FP8: four in flight), and a page
+// is processed as soon as it has landed, so once the stream ends only the last page's
+// work remains.
+//
+// Row block rb = t * head_groups + hg holds heads 16 hg .. 16 hg + 15 of query token t.
+// A problem with more than RBW row blocks runs row_groups = row blocks / RBW workgroups
+// per unit, each on the same pieces with its own row blocks.  They read the same pages:
+// the block index puts all row groups of a unit on one XCD (workgroups are dealt to the
+// eight XCDs by block index modulo 8) at about the same time, so the repeated reads of a
+// page are served by that XCD's L2 rather than HBM.
+template <bool FP8, int RBW>
 struct KSplitCfg {
   using TG = TileGeom<FP8>;
+  using QC = QueryCopy<8, RBW>;
   static constexpr int NW = 8;
   static constexpr int kTiles = FP8 ? 4 : 2;
   static constexpr int kPer = PageCopy<FP8, NW>::kPer;
   static constexpr int KS = kDLatent / 32 / 2;  // k-steps per half: 9
   static constexpr int CT = 4;                  // 16-column output tiles per wave
-  static constexpr int kQTiles =
-      (QueryCopy<NW, 1>::kBlocks * 1024 + TG::kPageBytes - 1) / TG::kPageBytes;
-  static_assert(kPer * kTiles + QueryCopy<NW, 1>::kPer <= 63, "outstanding operations exceed vmcnt");
+  static constexpr int kQTiles = (QC::kBlocks * 1024 + TG::kPageBytes - 1) / TG::kPageBytes;
+  static_assert(RBW == 1 || RBW == 2, "row blocks per workgroup");
+  static_assert(kPer * kTiles + QC::kPer <= 63, "outstanding operations exceed vmcnt");
   static_assert(kQTiles < kTiles, "tile plan");
 };
 
-template <bool FP8>
+template <bool FP8, int RBW>
 struct KSplitSmem {
-  using C = KSplitCfg<FP8>;
+  using C = KSplitCfg<FP8, RBW>;
   __attribute__((aligned(1024))) unsigned char tiles[C::kTiles * C::TG::kPageBytes];
-  f32x4 sx[4][64];                                               // k-half 1 partial scores
-  __attribute__((aligned(16))) unsigned char pbuf[2 * 64 * 16];  // P^T of the page, bf16
-  float red[4 * 16];                                             // row maxima of the sub-tiles
-  float red2[4 * 16];                                            // row denominators (epilogue)
+  f32x4 sx[RBW][4][64];                                               // k-half 1 partial scores
+  __attribute__((aligned(16))) unsigned char pbuf[RBW][2 * 64 * 16];  // P^T of the page, bf16
+  float red[RBW][4 * 16];                                             // row maxima of the sub-tiles
+  float red2[RBW][4 * 16];                                            // row denominators (epilogue)
 };
 
-template <bool FP8>
+// The (unit, row group) of this workgroup; false for a block past the last unit (the grid
+// is rounded up to whole groups of eight units when there are several row groups).
+__device__ __forceinline__ bool unit_of_block(int nwg, int rgroups, int64_t& w, int& g) {
+  if (rgroups == 1) {
+    w = blockIdx.x;
+    g = 0;
+    return true;
+  }
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int wb = q / rgroups;
+  g = q - wb * rgroups;
+  w = (int64_t)wb * 8 + xcd;
+  return w < nwg;
+}
+
+template <bool FP8, int RBW>
 __device__ __forceinline__ void partial_ks(
     const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    void* __restrict__ part_o, float* __restrict__ part_lse, KSplitSmem<FP8>& sm) {
-  using C = KSplitCfg<FP8>;
+    void* __restrict__ part_o, float* __restrict__ part_lse, KSplitSmem<FP8, RBW>& sm) {
+  using C = KSplitCfg<FP8, RBW>;
   using TG = TileGeom<FP8>;
   constexpr int kTiles = C::kTiles, kPer = C::kPer, CT = C::CT, KS = C::KS;
   constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
   const HotArgs args(p);
+  int64_t w;
+  int g;
+  if (!unit_of_block(args.nwg, args.rgroups, w, g)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int u = wave & 3, kh = wave >> 2;  // sub-tile, k-half
-  const int head = lrow;                   // one token: rows are the heads
-  const bool head_ok = head < args.heads;
+  // this workgroup's row blocks: token, output row of this lane's head, causal lag
+  int orow[RBW], lag[RBW];
+  bool head_ok[RBW];
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) {
+    const int rb = g * RBW + j;
+    const int t = rb / args.hgroups, hg = rb - t * args.hgroups;
+    const int head = hg * kRowsPerBlock + lrow;
+    head_ok[j] = head < args.heads;
+    orow[j] = t * args.heads + head;
+    lag[j] = args.causal ? args.qlen - 1 - t : 0;  // token t sees positions < L - lag
+  }
+  int lag_max = 0;
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) lag_max = max(lag_max, lag[j]);
   const PageCopy<FP8, C::NW> copy(wave, lane);
   const OperandAddr<FP8> addr(lrow, lgrp, 4 * wave);  // V^T: output column tiles 4w .. 4w+3
   unsigned char* const tiles = sm.tiles;
+  using SM = KSplitSmem<FP8, RBW>;
+  const uint32_t tiles_lds = lds_addr(sm.tiles);   // LDS base of the workgroup's object
+  const uint32_t red_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, red) - __builtin_offsetof(SM, tiles));
+  const uint32_t red2_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, red2) - __builtin_offsetof(SM, tiles));
+  const uint32_t pbuf_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, pbuf) - __builtin_offsetof(SM, tiles));
 
   auto run_piece = [&](int r, int pb, int pe, int64_t slot, int L) {
     const int32_t* trow = block_table + (int64_t)r * args.maxp;
@@ -851,13 +527,14 @@ __device__ __forceinline__ void partial_ks(
         bad = true;
         id = 0;
       }
-      copy(tiles + (i % kTiles) * TG::kPageBytes, pool + (int64_t)id * TG::kPageBytes,
+      copy(tiles_lds + (i % kTiles) * TG::kPageBytes, pool + (int64_t)id * TG::kPageBytes,
            min(kPage, L - lp * kPage));
     };
 
     // ---- queries through LDS (one HBM read per workgroup), then the first pages
     unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
-    QueryCopy<C::NW, 1>(wave, lane)(stage, q_ptr + (int64_t)r * args.heads * kDLatent, args.heads, 1);
+    typename C::QC(wave, lane)(tiles_lds + kEarlyTiles * TG::kPageBytes, q_ptr + (int64_t)r * args.qlen * args.heads * kDLatent, args.heads,
+                               args.hgroups, g * RBW);
     int early = 0;
 #pragma unroll
     for (int ti = 0; ti < kEarlyTiles; ++ti) {
@@ -866,24 +543,30 @@ __device__ __forceinline__ void partial_ks(
     }
     wait_pages<kPer, kEarlyTiles>(early);  // the query copies are older: all landed
     barrier_lds();
-    i32x4 qf[KS];  // this wave's half of the queries
-    {
+    i32x4 qf[RBW][KS];  // this wave's half of the queries of each row block
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const int kk = kh * KS + j;  // depends on the wave: offsets computed, not indexed
+    for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int kk = kh * KS + s;  // depends on the wave: offsets computed, not indexed
         const int kb = OperandAddr<false>::kbase_of(lrow, lgrp, kk & 1);
-        qf[j] = *(const i32x4*)(stage + kb + OperandAddr<false>::kstep(kk));
+        qf[j][s] = *(const i32x4*)(stage + j * kRowsPerBlock * TileGeom<false>::kRowBytes + kb +
+                                   OperandAddr<false>::kstep(kk));
       }
     }
     barrier_lds();  // the staging tiles are free again
 #pragma unroll
     for (int ti = kEarlyTiles; ti < kTiles; ++ti) issue(ti);
 
-    float m = kNegInf;  // running row max (log2 units), the same in every wave
-    float lsum = 0.f;   // k-half 0 waves: this lane's share of its sub-tile's denominator
-    f32x4 acc[CT];
+    float m[RBW], lsum[RBW];  // running row max (log2 units, the same in every wave) and,
+    f32x4 acc[RBW][CT];       // in k-half 0 waves, this lane's share of the denominator
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RBW; ++j) {
+      m[j] = kNegInf;
+      lsum[j] = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     for (int i = 0; i < n; ++i) {
       // pages i+1 .. i+kTiles-1 were issued after page i: let them fly
@@ -898,105 +581,154 @@ __device__ __forceinline__ void partial_ks(
       const unsigned char* kt = tile + u * 16 * TG::kRowBytes;
       bf16x8 kf[KS];
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const int kk = kh * KS + j;
+      for (int s = 0; s < KS; ++s) {
+        const int kk = kh * KS + s;
         const unsigned char* ka =
             kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1) + OperandAddr<FP8>::kstep(kk);
-        if constexpr (FP8) kf[j] = fp8x8_to_bf16x8(*(const i32x2*)ka);
-        else kf[j] = *(const bf16x8*)ka;
+        if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
+        else kf[s] = *(const bf16x8*)ka;
       }
-      f32x4 sp = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 sp[RBW];
 #pragma unroll
-      for (int j = 0; j < KS; ++j)
-        sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], __builtin_bit_cast(bf16x8, qf[j]), sp, 0, 0, 0);
+      for (int j = 0; j < RBW; ++j) sp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int j = 0; j < RBW; ++j)
+          sp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[j][s]),
+                                                          sp[j], 0, 0, 0);
+      }
       bf16x8 va[2][CT];
+      auto read_v = [&]() {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const unsigned char* va0 = tile + c * 32 * TG::kRowBytes + addr.vbase[ct] + OperandAddr<FP8>::vstep(ct);
-          if constexpr (FP8) {
-            va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
-          } else {
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
-            const bf16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
-            va[c][ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          for (int ct = 0; ct < CT; ++ct) {
+            const unsigned char* va0 =
+                tile + c * 32 * TG::kRowBytes + addr.vbase[ct] + OperandAddr<FP8>::vstep(ct);
+            if constexpr (FP8) {
+              va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
+            } else {
+              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
+              const bf16x4 hi =
+                  __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
+              va[c][ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
           }
         }
-      }
-      if constexpr (!FP8) {
+      };
+      // bf16 with two row blocks: no registers to spare for early V^T operands
+      constexpr bool kEarlyV = FP8 || RBW == 1;
+      if constexpr (kEarlyV) read_v();
+      if constexpr (!FP8 && RBW == 1) {
         // instruction order: six K reads ahead of the MFMAs, then one MFMA per remaining
         // read; the sixteen V^T reads go between the last six MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+        for (int s = 0; s < 3; ++s) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int s = 0; s < 4; ++s) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int s = 0; s < 2; ++s) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+      } else if constexpr (!FP8) {
+        // two row blocks: four K reads ahead, then one k-step's two MFMAs per remaining read
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s = 0; s < 5; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
 
       // ---- the k-halves meet: half 1 hands its partial scores to half 0, which scales,
       // masks and takes its sub-tile's row max
-      if (kh == 1) sm.sx[u][lane] = sp;
-      barrier_lds();
-      f32x4 sv = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-      if (kh == 0) {
-        const f32x4 other = sm.sx[u][lane];
-        float mx = kNegInf;
+      if (kh == 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = lp * kPage + u * 16 + lgrp * 4 + e;
-          const float v = j < L ? (sp[e] + other[e]) * args.sscale : kNegInf;
-          sv[e] = v;
-          mx = fmaxf(mx, v);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (lgrp == 0) sm.red[u * 16 + lrow] = mx;
+        for (int j = 0; j < RBW; ++j) sm.sx[j][u][lane] = sp[j];
       }
       barrier_lds();
-      const float mx = lds_max_of<4>(&sm.red[lrow], kNegInf);
-
-      // ---- online softmax update; half 0 builds P^T of its sub-tile for every wave
-      const float m_new = fmaxf(m, mx);
-      const float msub = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m - msub);  // m = -inf -> 0
-      m = m_new;
+      // raw scores (the scale is applied to the max and inside the exponent); positions
+      // at or past a row block's visible count are masked, which only a request's last
+      // pages need
+      f32x4 sv[RBW];
       if (kh == 0) {
-        float ps = 0.f;
+        const bool whole = (lp + 1) * kPage <= L - lag_max;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sv[e] = exp2_fast(sv[e] - msub);
-          ps += sv[e];
+        for (int j = 0; j < RBW; ++j) {
+          const f32x4 other = sm.sx[j][u][lane];
+          sv[j] = sp[j] + other;
+          if (!whole) {
+            const int vis = L - lag[j] - (lp * kPage + u * 16 + lgrp * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[j][e] = e < vis ? sv[j][e] : kNegInf;
+          }
+          float mx = fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3]));
+          mx = max_over_rows(mx);
+          if (lgrp == 0) sm.red[j][u * 16 + lrow] = mx * args.sscale;
         }
-        lsum = lsum * alpha + ps;
-        *(bf16x4*)(sm.pbuf + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
-            bf16x4{(__bf16)sv[0], (__bf16)sv[1], (__bf16)sv[2], (__bf16)sv[3]};
       }
       barrier_lds();
-      i32x4 p0, p1;
-      lds_read_pair_b128(sm.pbuf + lane * 16, p0, p1);
-      const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, p0), __builtin_bit_cast(bf16x8, p1)};
 
-      // ---- O^T += V^T P^T for this wave's 64 columns
+      // ---- online softmax update; half 0 builds P^T of its sub-tile for every wave.  The
+      // running max is exact (the largest weight of a row is exactly 1 in bf16); O is
+      // rescaled only on pages that raise some row's max, which become rare as the piece
+      // goes on.
+      float alpha[RBW];
+      bool grown = false;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] *= alpha;
+      for (int j = 0; j < RBW; ++j) {
+        const float mx = lds_max_of<4>(red_lds + 4 * (j * 64 + lrow), kNegInf);
+        const bool grow = mx > m[j];  // m = -inf: any finite max
+        const float m_new = grow ? mx : m[j];
+        const float msub = m_new == kNegInf ? 0.f : m_new;
+        alpha[j] = grow ? exp2_fast(m[j] - msub) : 1.f;  // m = -inf -> 0
+        grown |= grow;
+        m[j] = m_new;
+        if (kh == 0) {
+          float ps = 0.f;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+          for (int e = 0; e < 4; ++e) {
+            sv[j][e] = exp2_fast(fmaf(sv[j][e], args.sscale, -msub));
+            ps += sv[j][e];
+          }
+          lsum[j] = fmaf(lsum[j], alpha[j], ps);
+          *(bf16x4*)(sm.pbuf[j] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
+              bf16x4{(__bf16)sv[j][0], (__bf16)sv[j][1], (__bf16)sv[j][2], (__bf16)sv[j][3]};
+        }
+      }
+      // every lane of every wave sees the same maxima, so the branch is uniform
+      if (__builtin_amdgcn_ballot_w64(grown)) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[ct], 0, 0, 0);
+        for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[j][ct] *= alpha[j];
+        }
+      }
+      barrier_lds();
+
+      // ---- O^T += V^T P^T for this wave's 64 columns of every row block
+      if constexpr (!kEarlyV) read_v();
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+        i32x4 p0, p1;
+        lds_read_pair_b128(pbuf_lds + j * (2 * 64 * 16) + lane * 16, p0, p1);
+        const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, p0), __builtin_bit_cast(bf16x8, p1)};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[j][ct], 0, 0, 0);
+        }
       }
 
       // the next copy into this tile waits until every wave is done with it
@@ -1006,31 +738,35 @@ __device__ __forceinline__ void partial_ks(
       }
     }
 
-    // ---- epilogue: the row denominator from the four k-half 0 waves, normalise, store
-    float ls = lsum;
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    if (kh == 0 && lgrp == 0) sm.red2[u * 16 + lrow] = ls;
-    barrier_lds();
-    ls = lds_sum_of<4>(&sm.red2[lrow]);
-    const bool empty = m == kNegInf;
-    float oscale = empty ? 0.f : args.vscale / ls;
-    float lse = empty ? kNegInf : (m + log2_fast(ls)) * kLn2;
-    if (bad) {
-      oscale = __builtin_nanf("");
-      lse = __builtin_nanf("");
-    }
-    if (head_ok) {
+    // ---- epilogue: the row denominators from the four k-half 0 waves, normalise, store
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        store_partial(part_o, args.pbf16, head, 64 * wave + 16 * ct + 4 * lgrp, args.nslots, slot,
-                      acc[ct] * oscale);
-      if (wave == 0 && lgrp == 0) part_lse[(int64_t)head * args.nslots + slot] = lse;
+    for (int j = 0; j < RBW; ++j) {
+      const float ls = sum_over_rows(lsum[j]);
+      if (kh == 0 && lgrp == 0) sm.red2[j][u * 16 + lrow] = ls;
+    }
+    barrier_lds();
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+      const float ls = lds_sum_of<4>(red2_lds + 4 * (j * 64 + lrow));
+      const bool empty = m[j] == kNegInf;
+      float oscale = empty ? 0.f : args.vscale / ls;
+      float lse = empty ? kNegInf : (m[j] + log2_fast(ls)) * kLn2;
+      if (bad) {
+        oscale = __builtin_nanf("");
+        lse = __builtin_nanf("");
+      }
+      if (head_ok[j]) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          store_partial(part_o, args.pbf16, orow[j], 64 * wave + 16 * ct + 4 * lgrp, args.nslots, slot,
+                        acc[j][ct] * oscale);
+        if (wave == 0 && lgrp == 0) part_lse[(int64_t)orow[j] * args.nslots + slot] = lse;
+      }
     }
     barrier_lds();  // tiles and exchange buffers are reused by the next piece
   };
 
-  for_each_piece(p, args, seq_lens, run_piece);
+  for_each_piece(p, args, seq_lens, w, run_piece);
 }
 
 // ------------------------------------------------------------------- merge
@@ -1077,7 +813,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
   __shared__ float sm_acc[kMergeWaves][kTPS][kCPT];
   __shared__ float sm_den[kMergeWaves];
 
-  // scalar arguments of the prologue in one batch (see partial_phase)
+  // scalar arguments of the prologue in one batch (as HotArgs does for the partial stage)
   const int64_t a_rows = p.rows, a_total = p.total_pages;
   const int a_nwg = p.num_wg, a_nsplits = p.num_splits, a_mode = p.split_mode, a_plan_n = p.plan.n;
   const int a_nparts = p.num_parts, a_nslots = p.num_slots, a_len0 = p.plan.len[0];
@@ -1253,99 +989,47 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
 
 // ------------------------------------------------------------------- kernels
 
-// The workgroup shape for RB row blocks (see PartialCfg): one row block uses two groups
-// of 4 waves, two row blocks two groups of 2 waves per row block, so the four SIMDs each
-// run two waves; larger counts use one wave (two for three blocks) per row block.
-template <bool FP8, int RB>
-struct CfgFor;
-template <bool FP8> struct CfgFor<FP8, 2> { using type = PartialCfg<FP8, 2, 2, 2>; };
-template <bool FP8> struct CfgFor<FP8, 3> { using type = PartialCfg<FP8, 2, 3, 1>; };
-template <bool FP8> struct CfgFor<FP8, 4> { using type = PartialCfg<FP8, 1, 4, 1>; };
-template <bool FP8> struct CfgFor<FP8, 5> { using type = PartialCfg<FP8, 1, 5, 1>; };
-template <bool FP8> struct CfgFor<FP8, 6> { using type = PartialCfg<FP8, 1, 6, 1>; };
-template <bool FP8> struct CfgFor<FP8, 7> { using type = PartialCfg<FP8, 1, 7, 1>; };
-template <bool FP8> struct CfgFor<FP8, 8> { using type = PartialCfg<FP8, 1, 8, 1>; };
+constexpr int kPartialThreads = 512;
+static_assert(KSplitCfg<false, 1>::NW * 64 == kPartialThreads, "workgroup size");
 
-// LDS (the page tiles) caps residency at one workgroup per compute unit; the register
-// budget is what that workgroup's waves per SIMD allow.
-template <bool FP8, class C>
-__global__ __launch_bounds__(C::NW * 64)
-__attribute__((amdgpu_waves_per_eu((C::NW + 3) / 4, (C::NW + 3) / 4))) void mla_partial_kernel(
+// Eight waves, two per SIMD; the page tiles cap residency at one workgroup per compute
+// unit, so each wave may hold up to 256 registers.
+template <bool FP8, int RBW>
+__global__ __launch_bounds__(kPartialThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     void* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ PartialSmem<C> sm;
-  partial_phase<FP8, C>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
-}
-
-
-// One row block (one token, up to 16 heads): the K-split workgroup of eight waves.
-template <bool FP8>
-__global__ __launch_bounds__(KSplitCfg<FP8>::NW * 64)
-__attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_ks_kernel(
-    PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    void* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ KSplitSmem<FP8> sm;
-  partial_ks<FP8>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+  __shared__ KSplitSmem<FP8, RBW> sm;
+  partial_ks<FP8, RBW>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
 // ------------------------------------------------------------------ launchers
 
 namespace {
 
-template <bool FP8, class C>
+template <bool FP8, int RBW>
 hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_partial_kernel<FP8, C>), dim3(p.num_wg), dim3(C::NW * 64), 0, stream, p,
-                     p.q, p.pool, p.block_table, p.seq_lens, p.part_o, p.part_lse);
+  hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW>), dim3(partial_grid(p.num_wg, p.row_groups)),
+                     dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
+                     p.seq_lens, p.part_o, p.part_lse);
   return hipGetLastError();
 }
-
-template <bool FP8>
-hipError_t launch_partial_ks(const PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_partial_ks_kernel<FP8>), dim3(p.num_wg), dim3(KSplitCfg<FP8>::NW * 64), 0,
-                     stream, p, p.q, p.pool, p.block_table, p.seq_lens, p.part_o, p.part_lse);
-  return hipGetLastError();
-}
-
-// row blocks 2 .. 8 (one row block takes the K-split kernel)
-template <bool FP8, template <bool, class> class F, class... A>
-auto by_row_blocks(int rb, A&&... a) {
-  switch (rb) {
-    case 2: return F<FP8, typename CfgFor<FP8, 2>::type>::run(a...);
-    case 3: return F<FP8, typename CfgFor<FP8, 3>::type>::run(a...);
-    case 4: return F<FP8, typename CfgFor<FP8, 4>::type>::run(a...);
-    case 5: return F<FP8, typename CfgFor<FP8, 5>::type>::run(a...);
-    case 6: return F<FP8, typename CfgFor<FP8, 6>::type>::run(a...);
-    case 7: return F<FP8, typename CfgFor<FP8, 7>::type>::run(a...);
-    default: return F<FP8, typename CfgFor<FP8, 8>::type>::run(a...);
-  }
-}
-
-template <bool FP8, class C>
-struct PartialLaunch {
-  static hipError_t run(const PartialParams& p, hipStream_t s) { return launch_partial_t<FP8, C>(p, s); }
-};
-template <bool FP8, class C>
-struct PartialLds {
-  static size_t run() { return sizeof(PartialSmem<C>); }
-};
 
 }  // namespace
 
 // LDS bytes of one partial-stage workgroup, for the planner's residency estimate.
-size_t partial_lds_size(bool fp8, int row_blocks) {
-  if (row_blocks < 1 || row_blocks > kMaxRowBlocks) return 0;
-  if (row_blocks == 1) return fp8 ? sizeof(KSplitSmem<true>) : sizeof(KSplitSmem<false>);
-  return fp8 ? by_row_blocks<true, PartialLds>(row_blocks) : by_row_blocks<false, PartialLds>(row_blocks);
+size_t partial_lds_size(bool fp8, int rbw) {
+  if (rbw == 1) return fp8 ? sizeof(KSplitSmem<true, 1>) : sizeof(KSplitSmem<false, 1>);
+  if (rbw == 2) return fp8 ? sizeof(KSplitSmem<true, 2>) : sizeof(KSplitSmem<false, 2>);
+  return 0;
 }
 
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream) {
-  const int rb = p.q_len * p.head_groups;
-  if (rb < 1 || rb > kMaxRowBlocks) return hipErrorInvalidValue;
-  if (rb == 1) return fp8 ? launch_partial_ks<true>(p, stream) : launch_partial_ks<false>(p, stream);
-  return fp8 ? by_row_blocks<true, PartialLaunch>(rb, p, stream)
-             : by_row_blocks<false, PartialLaunch>(rb, p, stream);
+  if (p.row_groups < 1 || p.rbw * p.row_groups != p.q_len * p.head_groups) return hipErrorInvalidValue;
+  if (p.rbw == 1) return fp8 ? launch_partial_t<true, 1>(p, stream) : launch_partial_t<false, 1>(p, stream);
+  if (p.rbw == 2) return fp8 ? launch_partial_t<true, 2>(p, stream) : launch_partial_t<false, 2>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,

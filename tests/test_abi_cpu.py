@@ -91,9 +91,12 @@ def test_plan_argument_checks():
     assert plan_status(page=32) == U
     assert plan_status(dtype=mb.MLA_FP32) == U
     assert plan_status(q_len=4, seq_lens=(3,)) == E  # seq_len < q_len
-    assert plan_status(heads=129) == U  # 9 row blocks
-    assert plan_status(q_len=3, heads=48, seq_lens=(100,)) == U  # 9 row blocks
+    assert plan_status(heads=129) == mb.MLA_OK  # 9 row blocks
+    assert plan_status(q_len=3, heads=48, seq_lens=(100,)) == mb.MLA_OK  # 9 row blocks
     assert plan_status(q_len=8, heads=16, seq_lens=(100,)) == mb.MLA_OK
+    assert plan_status(q_len=4, heads=256, seq_lens=(100,)) == mb.MLA_OK  # 64 row blocks
+    assert plan_status(heads=1025) == U  # 65 row blocks
+    assert plan_status(q_len=5, heads=208, seq_lens=(100,)) == U  # 65 row blocks
     assert plan_status(cus=-1) == E
     assert plan_status(partial=1) == mb.MLA_OK
     assert plan_status(partial=2) == E
@@ -171,9 +174,15 @@ def check_plan(seq_lens, q_len=1, heads=16, splits=0, cus=256, dtype=mb.MLA_BF16
     assert len(set(work[:, 4])) == len(work)
     assert work[:, 4].min() >= 0 and work[:, 4].max() < S
     assert set(work[:, 0]) <= set(range(W))
+    rb = q_len * -(-heads // 16)
+    G = rb // 2 if rb % 2 == 0 else rb  # row blocks go two to a workgroup when they pair up
+    assert plan.row_groups == G
     if splits == 0:
         P = sum(pages)
-        assert min(P, cus) <= W <= min(P, 2 * cus)  # every compute unit busy when possible
+        # every compute unit busy when possible; with several row groups, whole units per
+        # XCD (eight XCDs)
+        target = cus if G == 1 else (8 * (cus // 8 // G) if cus // 8 >= G else cus // G)
+        assert W == min(P, max(1, target))
         per_wg = np.zeros(W, dtype=np.int64)
         for w, _, pb, pe, _ in work:
             per_wg[w] += pe - pb
@@ -203,7 +212,10 @@ def test_planner_named_workloads(name):
     for splits in {0, spec["num_splits"]}:
         plan, _ = check_plan(list(seq_lens), spec["q_len"], spec["num_heads"], splits, dtype=dtype)
         if splits == 0:
-            assert plan.num_units >= min(256, sum(-(-int(L) // 64) for L in seq_lens))
+            P = sum(-(-int(L) // 64) for L in seq_lens)
+            G = plan.row_groups
+            assert plan.num_units == min(P, 256 if G == 1 else 8 * (32 // G))
+            assert plan.num_units * G <= 256
     # the named counts the pages give: 16 partitions per request, 4 for the tiny case
     if spec["num_splits"]:
         plan = mb.Plan(spec["batch"], spec["q_len"], spec["num_heads"], list(seq_lens), TAU,
@@ -224,6 +236,14 @@ def test_planner_invariants(seq_lens, cus):
     check_plan(seq_lens, cus=cus)
     check_plan(seq_lens, splits=3, cus=cus)
     check_plan(seq_lens, splits=16, cus=cus)
+
+
+@pytest.mark.parametrize("q_len,heads", [(4, 16), (1, 96), (3, 16), (2, 96), (4, 256)])
+@pytest.mark.parametrize("cus", [1, 7, 100, 256])
+def test_planner_row_groups(q_len, heads, cus):
+    seq_lens = [max(q_len, L) for L in (17750, 3, 700, 64)]
+    check_plan(seq_lens, q_len=q_len, heads=heads, cus=cus)
+    check_plan(seq_lens, q_len=q_len, heads=heads, splits=5, cus=cus)
 
 
 @pytest.mark.parametrize("partials_bf16,elem", [(True, 2), (False, 4)])

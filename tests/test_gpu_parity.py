@@ -113,6 +113,15 @@ SMALL = [
     (2, 4, 16, [4, 70], 0, "fp8_e4m3fn"),
     (3, 1, 12, [1, 64, 129], 5, "fp8_e4m3fn"),
     (1, 2, 48, [200], 0, "fp8_e4m3fn"),
+    # odd row-block counts (one row block per workgroup), more than eight row blocks,
+    # and several row groups under fixed splits
+    (1, 3, 16, [150], 0, "bf16"),
+    (2, 5, 16, [300, 70], 0, "bf16"),
+    (2, 7, 16, [64, 500], 2, "bf16"),
+    (1, 3, 48, [200], 0, "fp8_e4m3fn"),
+    (2, 2, 96, [300, 100], 0, "bf16"),
+    (2, 2, 96, [300, 100], 3, "fp8_e4m3fn"),
+    (1, 4, 256, [130], 0, "bf16"),
 ]
 
 
