@@ -415,15 +415,16 @@ __device__ __forceinline__ void store_partial(void* part_o, bool bf16, int64_t o
 // ------------------------------------------------------------------- partial stage
 //
 // A workgroup of eight waves owns RBW row blocks of 16 query rows (RBW = 1 or 2) and the
-// pieces of one work unit; all eight waves work on the same page.  In QK^T wave w
-// computes the partial scores of the 16-position sub-tile u = w & 3 over half kh = w >> 2
-// of the latent (nine of the 18 k-steps of 32 columns) for each of its row blocks: every K
-// operand read from LDS serves all of them.  The two halves are added through LDS.  In
-// PV wave w produces output columns [64 w, 64 w + 64) of every row block over the page's
-// 64 positions, every V^T operand read serving all row blocks.  One softmax state per row
-// block for the whole workgroup, pages double-buffered (FP8: four in flight), and a page
-// is processed as soon as it has landed, so once the stream ends only the last page's
-// work remains.
+// pieces of one work unit; all eight waves work on the same page.  In QK^T, with one row
+// block, wave w computes the partial scores of the 16-position sub-tile u = w & 3 over
+// half kh = w >> 2 of the latent (nine of the 18 k-steps of 32 columns), and the two
+// halves are added through LDS; with two row blocks ("row split"), wave w computes the
+// whole scores of sub-tile u for row block w >> 2, so every wave then takes its share of
+// the softmax and no partial scores are exchanged.  In PV wave w produces output columns
+// [64 w, 64 w + 64) of every row block over the page's 64 positions, every V^T operand
+// read serving all row blocks.  One softmax state per row block for the whole workgroup,
+// pages double-buffered (FP8: four in flight), and a page is processed as soon as it has
+// landed, so once the stream ends only the last page's work remains.
 //
 // Row block rb = t * head_groups + hg holds heads 16 hg .. 16 hg + 15 of query token t.
 // A problem with more than RBW row blocks runs row_groups = row blocks / RBW workgroups
@@ -450,7 +451,7 @@ template <bool FP8, int RBW>
 struct KSplitSmem {
   using C = KSplitCfg<FP8, RBW>;
   __attribute__((aligned(1024))) unsigned char tiles[C::kTiles * C::TG::kPageBytes];
-  f32x4 sx[RBW][4][64];                                               // k-half 1 partial scores
+  f32x4 sx[RBW == 2 ? 1 : RBW][4][64];  // k-half 1 partial scores (not used with two row blocks)
   __attribute__((aligned(16))) unsigned char pbuf[RBW][2 * 64 * 16];  // P^T of the page, bf16
   float red[RBW][4 * 16];                                             // row maxima of the sub-tiles
   float red2[RBW][4 * 16];                                            // row denominators (epilogue)
@@ -471,7 +472,7 @@ __device__ __forceinline__ bool unit_of_block(int nwg, int rgroups, int64_t& w, 
   return w < nwg;
 }
 
-template <bool FP8, int RBW>
+template <bool FP8, int RBW, bool RS>
 __device__ __forceinline__ void partial_ks(
     const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -479,6 +480,12 @@ __device__ __forceinline__ void partial_ks(
   using C = KSplitCfg<FP8, RBW>;
   using TG = TileGeom<FP8>;
   constexpr int kTiles = C::kTiles, kPer = C::kPer, CT = C::CT, KS = C::KS;
+  // RS (two row blocks): wave w takes sub-tile w & 3 of row block w >> 2 over the whole
+  // latent instead of both row blocks over half of it: no partial-score exchange, and
+  // every wave shares the softmax work
+  static_assert(!RS || RBW == 2, "row split needs two row blocks");
+  constexpr int KQ = RS ? 2 * KS : KS;  // k-steps of queries a wave holds
+  constexpr int NQ = RS ? 1 : RBW;      // row blocks whose queries a wave holds
   constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
   const HotArgs args(p);
   int64_t w;
@@ -543,14 +550,15 @@ __device__ __forceinline__ void partial_ks(
     }
     wait_pages<kPer, kEarlyTiles>(early);  // the query copies are older: all landed
     barrier_lds();
-    i32x4 qf[RBW][KS];  // this wave's half of the queries of each row block
+    i32x4 qf[NQ][KQ];  // this wave's queries: half of each row block's, or all of one
 #pragma unroll
-    for (int j = 0; j < RBW; ++j) {
+    for (int j = 0; j < NQ; ++j) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int kk = kh * KS + s;  // depends on the wave: offsets computed, not indexed
+      for (int s = 0; s < KQ; ++s) {
+        const int kk = RS ? s : kh * KS + s;  // depends on the wave: offsets computed, not indexed
+        const int jr = RS ? kh : j;
         const int kb = OperandAddr<false>::kbase_of(lrow, lgrp, kk & 1);
-        qf[j][s] = *(const i32x4*)(stage + j * kRowsPerBlock * TileGeom<false>::kRowBytes + kb +
+        qf[j][s] = *(const i32x4*)(stage + jr * kRowsPerBlock * TileGeom<false>::kRowBytes + kb +
                                    OperandAddr<false>::kstep(kk));
       }
     }
@@ -558,8 +566,9 @@ __device__ __forceinline__ void partial_ks(
 #pragma unroll
     for (int ti = kEarlyTiles; ti < kTiles; ++ti) issue(ti);
 
-    float m[RBW], lsum[RBW];  // running row max (log2 units, the same in every wave) and,
-    f32x4 acc[RBW][CT];       // in k-half 0 waves, this lane's share of the denominator
+    float m[RBW], lsum[RBW];  // running row max (log2 units, the same in every wave) and
+    f32x4 acc[RBW][CT];       // this lane's share of the denominator (k-half 0 waves; RS:
+                              // lsum[0], of the wave's own row block)
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
       m[j] = kNegInf;
@@ -579,10 +588,10 @@ __device__ __forceinline__ void partial_ks(
       // this wave's output columns (both 32-position chunks; they do not depend on the
       // softmax, so these transposing reads run under the MFMAs and the exchanges)
       const unsigned char* kt = tile + u * 16 * TG::kRowBytes;
-      bf16x8 kf[KS];
+      bf16x8 kf[KQ];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int kk = kh * KS + s;
+      for (int s = 0; s < KQ; ++s) {
+        const int kk = RS ? s : kh * KS + s;
         const unsigned char* ka =
             kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1) + OperandAddr<FP8>::kstep(kk);
         if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
@@ -591,12 +600,21 @@ __device__ __forceinline__ void partial_ks(
       f32x4 sp[RBW];
 #pragma unroll
       for (int j = 0; j < RBW; ++j) sp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (RS) {
+        // two accumulators (even and odd k-steps) halve the dependent MFMA chain
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KQ; ++s)
+          sp[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[0][s]),
+                                                              sp[s & 1], 0, 0, 0);
+        sp[0] += sp[1];
+      } else {
 #pragma unroll
-        for (int j = 0; j < RBW; ++j)
-          sp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[j][s]),
-                                                          sp[j], 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+          for (int j = 0; j < RBW; ++j)
+            sp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[j][s]),
+                                                            sp[j], 0, 0, 0);
+        }
       }
       bf16x8 va[2][CT];
       auto read_v = [&]() {
@@ -620,7 +638,16 @@ __device__ __forceinline__ void partial_ks(
       // bf16 with two row blocks: no registers to spare for early V^T operands
       constexpr bool kEarlyV = FP8 || RBW == 1;
       if constexpr (kEarlyV) read_v();
-      if constexpr (!FP8 && RBW == 1) {
+      if constexpr (!FP8 && RS) {
+        // four K reads ahead of the MFMAs, then one MFMA per remaining read
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s = 0; s < KQ - 4; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      } else if constexpr (!FP8 && RBW == 1) {
         // instruction order: six K reads ahead of the MFMAs, then one MFMA per remaining
         // read; the sixteen V^T reads go between the last six MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
@@ -651,17 +678,29 @@ __device__ __forceinline__ void partial_ks(
       }
 
       // ---- the k-halves meet: half 1 hands its partial scores to half 0, which scales,
-      // masks and takes its sub-tile's row max
-      if (kh == 1) {
+      // masks and takes its sub-tile's row max (RS: every wave has whole scores)
+      if constexpr (!RS) {
+        if (kh == 1) {
 #pragma unroll
-        for (int j = 0; j < RBW; ++j) sm.sx[j][u][lane] = sp[j];
+          for (int j = 0; j < RBW; ++j) sm.sx[j][u][lane] = sp[j];
+        }
+        barrier_lds();
       }
-      barrier_lds();
       // raw scores (the scale is applied to the max and inside the exponent); positions
       // at or past a row block's visible count are masked, which only a request's last
       // pages need
       f32x4 sv[RBW];
-      if (kh == 0) {
+      if constexpr (RS) {
+        sv[0] = sp[0];
+        if ((lp + 1) * kPage > L - lag_max) {
+          const int vis = L - (kh ? lag[RBW - 1] : lag[0]) - (lp * kPage + u * 16 + lgrp * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[0][e] = e < vis ? sv[0][e] : kNegInf;
+        }
+        float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+        mx = max_over_rows(mx);
+        if (lgrp == 0) sm.red[kh][u * 16 + lrow] = mx * args.sscale;
+      } else if (kh == 0) {
         const bool whole = (lp + 1) * kPage <= L - lag_max;
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
@@ -683,7 +722,7 @@ __device__ __forceinline__ void partial_ks(
       // running max is exact (the largest weight of a row is exactly 1 in bf16); O is
       // rescaled only on pages that raise some row's max, which become rare as the piece
       // goes on.
-      float alpha[RBW];
+      float alpha[RBW], msubs[RBW];
       bool grown = false;
 #pragma unroll
       for (int j = 0; j < RBW; ++j) {
@@ -691,10 +730,11 @@ __device__ __forceinline__ void partial_ks(
         const bool grow = mx > m[j];  // m = -inf: any finite max
         const float m_new = grow ? mx : m[j];
         const float msub = m_new == kNegInf ? 0.f : m_new;
+        msubs[j] = msub;
         alpha[j] = grow ? exp2_fast(m[j] - msub) : 1.f;  // m = -inf -> 0
         grown |= grow;
         m[j] = m_new;
-        if (kh == 0) {
+        if (!RS && kh == 0) {
           float ps = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -705,6 +745,18 @@ __device__ __forceinline__ void partial_ks(
           *(bf16x4*)(sm.pbuf[j] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
               bf16x4{(__bf16)sv[j][0], (__bf16)sv[j][1], (__bf16)sv[j][2], (__bf16)sv[j][3]};
         }
+      }
+      if constexpr (RS) {  // this wave's sub-tile of its row block
+        const float msub = kh ? msubs[RBW - 1] : msubs[0];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[0][e] = exp2_fast(fmaf(sv[0][e], args.sscale, -msub));
+          ps += sv[0][e];
+        }
+        lsum[0] = fmaf(lsum[0], kh ? alpha[RBW - 1] : alpha[0], ps);
+        *(bf16x4*)(sm.pbuf[kh] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
+            bf16x4{(__bf16)sv[0][0], (__bf16)sv[0][1], (__bf16)sv[0][2], (__bf16)sv[0][3]};
       }
       // every lane of every wave sees the same maxima, so the branch is uniform
       if (__builtin_amdgcn_ballot_w64(grown)) {
@@ -739,10 +791,15 @@ __device__ __forceinline__ void partial_ks(
     }
 
     // ---- epilogue: the row denominators from the four k-half 0 waves, normalise, store
+    if constexpr (RS) {
+      const float ls = sum_over_rows(lsum[0]);
+      if (lgrp == 0) sm.red2[kh][u * 16 + lrow] = ls;
+    } else {
 #pragma unroll
-    for (int j = 0; j < RBW; ++j) {
-      const float ls = sum_over_rows(lsum[j]);
-      if (kh == 0 && lgrp == 0) sm.red2[j][u * 16 + lrow] = ls;
+      for (int j = 0; j < RBW; ++j) {
+        const float ls = sum_over_rows(lsum[j]);
+        if (kh == 0 && lgrp == 0) sm.red2[j][u * 16 + lrow] = ls;
+      }
     }
     barrier_lds();
 #pragma unroll
@@ -1001,7 +1058,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     void* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ KSplitSmem<FP8, RBW> sm;
-  partial_ks<FP8, RBW>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+  partial_ks<FP8, RBW, RBW == 2>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
 // ------------------------------------------------------------------ launchers
