@@ -17,7 +17,7 @@
 namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
-                        hipStream_t stream);
+                        int max_row_slots, hipStream_t stream);
 size_t partial_lds_size(bool fp8, int rbw);
 }  // namespace mla
 
@@ -40,6 +40,7 @@ struct mla_plan {
   int32_t part_bf16;     // partial O element type
   int64_t total_pages;
   int32_t max_req_pages;  // largest ceil(seq_len / page) of a request
+  int32_t max_req_slots;  // most partial answers of one request
   size_t o_offset, o_bytes, lse_offset, workspace_bytes;
   std::vector<int32_t> seq_lens;  // host copy, for get_work only
 };
@@ -225,6 +226,18 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   }
   pl->num_wg = (int32_t)wg;
   pl->num_slots = (int32_t)slots;
+  if (pl->mode == SPLIT_FIXED) {
+    pl->max_req_slots = pl->num_splits;
+  } else {
+    int64_t pre = 0, most = 0;
+    for (int32_t r = 0; r < s.batch; ++r) {
+      const int64_t pr = pages_of(seq_lens_host[r], INT32_MAX);
+      const int64_t n = balanced_wg_of(pre + pr - 1, total_pages, wg) - balanced_wg_of(pre, total_pages, wg) + 1;
+      if (n > most) most = n;
+      pre += pr;
+    }
+    pl->max_req_slots = (int32_t)most;
+  }
   pl->part_bf16 = s.partials_bf16;
   // [partial O | fp32 partial LSE], each 256-byte aligned
   pl->o_offset = 0;
@@ -378,7 +391,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
     e = launch_partial(pp, fp8, st);
     if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
   }
-  e = launch_merge(mp, plan->part_bf16, true, (int64_t)s.batch * plan->rows, st);
+  e = launch_merge(mp, plan->part_bf16, true, (int64_t)s.batch * plan->rows, plan->max_req_slots, st);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -405,7 +418,7 @@ mla_status mla_merge_lse(const void* part_o, int32_t part_dtype, const float* pa
   mp.rows = rows;
   mp.out_bf16 = out_dtype == MLA_BF16;
   mp.num_parts = num_parts;
-  hipError_t e = launch_merge(mp, part_dtype == MLA_BF16, false, rows, (hipStream_t)stream);
+  hipError_t e = launch_merge(mp, part_dtype == MLA_BF16, false, rows, num_parts, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }

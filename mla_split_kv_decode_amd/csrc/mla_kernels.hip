@@ -862,6 +862,50 @@ __device__ __forceinline__ void load_piece(const void* base, int64_t idx, float 
   }
 }
 
+// Slot range [s0, s1) of request grp's partial answers.  Under SPLIT_BALANCED every work
+// unit owns at least one page (W <= P), so every slot in the range holds a piece.  On the
+// plan path the device length (a vector load, waited for only where it is compared, after
+// the partial answers have been loaded) must equal the plan's: the caller compares
+// dev_len with plan_len.
+__device__ __forceinline__ void decode_slots(const MergeParams& p, int64_t grp, int plan_n, int mode,
+                                             int nsplits, int nwg, int64_t total, int len0,
+                                             int64_t& s0, int64_t& s1, bool& inconsistent,
+                                             int& dev_len, int& plan_len) {
+  if (plan_n == 1) {  // one request
+    dev_len = vector_load_i32(p.seq_lens);
+    plan_len = len0;
+    s1 = mode == SPLIT_FIXED ? nsplits : nwg;
+  } else if (plan_n > 0) {
+    // slot range from the plan's lengths; the device length is only compared with it
+    dev_len = vector_load_i32(p.seq_lens + grp);
+    plan_len = p.plan.len[grp];
+    if (mode == SPLIT_FIXED) {
+      s0 = grp * nsplits;
+      s1 = s0 + nsplits;
+    } else {
+      const int64_t pre = p.plan.pre[grp], pr = p.plan.pre[grp + 1] - pre;
+      s0 = balanced_wg_of(pre, total, nwg) + grp;
+      s1 = balanced_wg_of(pre + pr - 1, total, nwg) + grp + 1;
+    }
+  } else if (mode == SPLIT_FIXED) {
+    s0 = grp * nsplits;
+    s1 = s0 + nsplits;
+  } else {
+    int64_t P = 0, pre = 0, pr = 0;
+    for (int r = 0; r < p.batch; ++r) {
+      const int pg = pages_of(p.seq_lens[r], p.max_pages);
+      if (r < grp) pre += pg;
+      if (r == grp) pr = pg;
+      P += pg;
+    }
+    inconsistent = P != p.total_pages;
+    if (pr > 0 && !inconsistent) {
+      s0 = balanced_wg_of(pre, P, p.num_wg) + grp;
+      s1 = balanced_wg_of(pre + pr - 1, P, p.num_wg) + grp + 1;
+    }
+  }
+}
+
 template <bool PART_BF16, bool OUT_BF16, bool DECODE>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p) {
   using MG = MergeGeom<PART_BF16>;
@@ -886,48 +930,12 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
   const int64_t grp = (int64_t)((uint32_t)orow / (uint32_t)a_rows);  // rows * groups < 2^31
   const int64_t row = orow - grp * a_rows;
 
-  // slot range [s0, s1) of this group.  Under SPLIT_BALANCED every workgroup owns at
-  // least one page (W <= P), so every slot in the range holds a piece.
+  // slot range [s0, s1) of this group
   int64_t s0 = 0, s1 = 0;
   bool inconsistent = false;
-  // plan path: the device length (a vector load, waited for only where it is compared,
-  // after the partial answers have been loaded) must equal the plan's
   int dev_len = 0, plan_len = 0;
-  if constexpr (!DECODE) {
-    s1 = a_nparts;
-  } else if (a_plan_n == 1) {  // one request
-    dev_len = vector_load_i32(p.seq_lens);
-    plan_len = a_len0;
-    s1 = a_mode == SPLIT_FIXED ? a_nsplits : a_nwg;
-  } else if (a_plan_n > 0) {
-    // slot range from the plan's lengths; the device length is only compared with it
-    dev_len = vector_load_i32(p.seq_lens + grp);
-    plan_len = p.plan.len[grp];
-    if (a_mode == SPLIT_FIXED) {
-      s0 = grp * a_nsplits;
-      s1 = s0 + a_nsplits;
-    } else {
-      const int64_t pre = p.plan.pre[grp], pr = p.plan.pre[grp + 1] - pre;
-      s0 = balanced_wg_of(pre, a_total, a_nwg) + grp;
-      s1 = balanced_wg_of(pre + pr - 1, a_total, a_nwg) + grp + 1;
-    }
-  } else if (a_mode == SPLIT_FIXED) {
-    s0 = grp * a_nsplits;
-    s1 = s0 + a_nsplits;
-  } else {
-    int64_t P = 0, pre = 0, pr = 0;
-    for (int r = 0; r < p.batch; ++r) {
-      const int pg = pages_of(p.seq_lens[r], p.max_pages);
-      if (r < grp) pre += pg;
-      if (r == grp) pr = pg;
-      P += pg;
-    }
-    inconsistent = P != p.total_pages;
-    if (pr > 0 && !inconsistent) {
-      s0 = balanced_wg_of(pre, P, p.num_wg) + grp;
-      s1 = balanced_wg_of(pre + pr - 1, P, p.num_wg) + grp + 1;
-    }
-  }
+  if constexpr (!DECODE) s1 = a_nparts;
+  else decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, s0, s1, inconsistent, dev_len, plan_len);
   const int64_t col = (int64_t)chunk * kMergeCols + cp * kCPT;
   auto o_index = [&](int64_t s) -> int64_t {
     if constexpr (DECODE) return ((row * kMergeChunks + chunk) * a_nslots + s) * kMergeCols + cp * kCPT;
@@ -1044,6 +1052,80 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
   }
 }
 
+// Row-wise merge, for plans whose rows have at most kRowSlots partial answers each (many
+// rows, few pieces per request: multi-token verification, large batches, DCP shards).
+// Two waves per output row, each lane owning 4 of the 512 columns; all of a row's partial
+// answers and LSEs are loaded in one round trip, the LSE maximum and the weights are
+// reduced across the wave's lanes, and each lane forms its columns' weighted sum.  Block
+// b serves rows 2b and 2b + 1 (one per pair of waves).
+constexpr int kRowSlots = 32;
+
+template <bool PART_BF16, bool OUT_BF16, bool DECODE>
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MergeParams p, int64_t total_rows) {
+  const int64_t a_rows = p.rows, a_total = p.total_pages;
+  const int a_nwg = p.num_wg, a_nsplits = p.num_splits, a_mode = p.split_mode, a_plan_n = p.plan.n;
+  const int a_nparts = p.num_parts, a_nslots = p.num_slots, a_len0 = p.plan.len[0];
+  asm volatile("" ::"s"(a_rows), "s"(a_total), "s"(a_nwg), "s"(a_nsplits), "s"(a_mode), "s"(a_plan_n),
+               "s"(a_nparts), "s"(a_nslots), "s"(a_len0));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t orow = 2 * (int64_t)blockIdx.x + (wave >> 1);
+  if (orow >= total_rows) return;  // the whole wave
+  const int col = (wave & 1) * 256 + lane * 4;
+  const int64_t grp = (int64_t)((uint32_t)orow / (uint32_t)a_rows);  // rows * groups < 2^31
+  const int64_t row = orow - grp * a_rows;
+
+  int64_t s0 = 0, s1 = 0;
+  bool inconsistent = false;
+  int dev_len = 0, plan_len = 0;
+  if constexpr (!DECODE) s1 = a_nparts;
+  else decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, s0, s1, inconsistent, dev_len, plan_len);
+  const int ns = (int)(s1 - s0);
+  auto o_index = [&](int64_t s) -> int64_t {
+    if constexpr (DECODE) return ((row * kMergeChunks + (col >> 5)) * a_nslots + s) * kMergeCols + (col & 31);
+    else return (s * a_rows + row) * kDV + col;
+  };
+  // all loads of the row at once: lane k < ns holds LSE of slot s0 + k
+  const float l = lane < ns ? p.part_lse[DECODE ? row * a_nslots + s0 + lane : (s0 + lane) * a_rows + row]
+                            : kNegInf;
+  f32x4 o[kRowSlots];
+#pragma unroll
+  for (int k = 0; k < kRowSlots; ++k) {
+    if (k < ns) {  // uniform
+      if constexpr (PART_BF16) {
+        const bf16x4 b = *(const bf16x4*)((const __bf16*)p.part_o + o_index(s0 + k));
+        o[k] = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+      } else {
+        o[k] = *(const f32x4*)((const float*)p.part_o + o_index(s0 + k));
+      }
+    }
+  }
+  inconsistent = inconsistent || dev_len != plan_len || ns > kRowSlots;
+  float M = l;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = nan_max(M, __shfl_xor(M, off));
+  const float a = M == kNegInf ? 0.f : exp2_fast((l - M) * kLog2e);  // lanes past ns: 0
+  float den = a;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kRowSlots; ++k) {
+    if (k < ns) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), k)) * o[k];
+  }
+  const bool empty = M == kNegInf && !inconsistent;
+  f32x4 v = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.0f / den);
+  if (inconsistent) v = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+  if (p.out) {
+    const int64_t off = orow * kDV + col;
+    if constexpr (OUT_BF16)
+      *(bf16x4*)((__bf16*)p.out + off) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    else
+      *(f32x4*)((float*)p.out + off) = v;
+  }
+  if (p.out_lse && (wave & 1) == 0 && lane == 0)
+    p.out_lse[orow] = inconsistent ? __builtin_nanf("") : (empty ? kNegInf : M + log2_fast(den) * kLn2);
+}
+
 // ------------------------------------------------------------------- kernels
 
 constexpr int kPartialThreads = 512;
@@ -1090,9 +1172,26 @@ hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream) 
 }
 
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
-                        hipStream_t stream) {
-  const dim3 grid((unsigned)(total_rows * kMergeChunks));
+                        int max_row_slots, hipStream_t stream) {
   const int sel = (part_bf16 ? 4 : 0) + (p.out_bf16 ? 2 : 0) + (decode ? 1 : 0);
+  if (max_row_slots <= kRowSlots) {
+    const dim3 grid((unsigned)((total_rows + 1) / 2));
+    switch (sel) {
+#define MLA_MERGE_CASE(S, A, B, D) \
+      case S: hipLaunchKernelGGL((mla_merge_rows_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, p, total_rows); break;
+      MLA_MERGE_CASE(0, false, false, false)
+      MLA_MERGE_CASE(1, false, false, true)
+      MLA_MERGE_CASE(2, false, true, false)
+      MLA_MERGE_CASE(3, false, true, true)
+      MLA_MERGE_CASE(4, true, false, false)
+      MLA_MERGE_CASE(5, true, false, true)
+      MLA_MERGE_CASE(6, true, true, false)
+      MLA_MERGE_CASE(7, true, true, true)
+#undef MLA_MERGE_CASE
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)(total_rows * kMergeChunks));
   switch (sel) {
 #define MLA_MERGE_CASE(S, A, B, D) \
     case S: hipLaunchKernelGGL((mla_merge_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, p); break;

@@ -258,11 +258,13 @@ def test_dcp_shard_merge():
             "device merge of 8 shards")
 
 
-def test_merge_lse_api():
+@pytest.mark.parametrize("P", [7, 32, 33, 300])
+def test_merge_lse_api(P):
+    """Both merge shapes: up to 32 parts a row runs row-wise, more by column chunks."""
     import torch
 
-    rng = np.random.default_rng(302)
-    P, R = 7, 40
+    rng = np.random.default_rng(302 + P)
+    R = 40
     o = rng.standard_normal((P, R, 512))
     l = rng.standard_normal((P, R)) * 3
     l[2, :5] = -np.inf
