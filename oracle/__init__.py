@@ -15,7 +15,9 @@ blog post, three translations).  Sections used:
 * section 4 "MLA: AITER assembly long-context decode": query heads attend to the
   cached positions independently (padding heads changes no real head), and the
   history may be split into partitions whose results are combined, with the KV
-  storage unchanged.
+  storage unchanged;
+* section 1 "Cache" (payload estimate): one 576-value latent per position and layer,
+  stored in FP8, appended to as the conversation grows (``cache.py``).
 
 Every function says which of these it follows.  Where the pages are silent the
 reading taken is stated in the docstring.  Parity is pinned in
@@ -24,6 +26,7 @@ library routines and the pages' own worked numbers.
 """
 
 from .numerics import bf16_bits_to_f64, e4m3fn_codes_to_f64
+from .cache import kv_append, quantize_e4m3fn, stored_row
 from .attention import (
     D_LATENT,
     D_V,
@@ -43,5 +46,8 @@ __all__ = [
     "decode_paged",
     "e4m3fn_codes_to_f64",
     "gather_latents",
+    "kv_append",
     "merge",
+    "quantize_e4m3fn",
+    "stored_row",
 ]

@@ -425,3 +425,155 @@ def test_causal_mutants_fail():
     assert pin_causal_drafts(shifted(0)) == []
     assert pin_causal_drafts(shifted(-1)) != []
     assert pin_causal_drafts(shifted(+1)) != []
+
+
+# --------------------------------------------------- P7 cache append, FP8 quantiser
+#
+# Kimi K3 on MI355X, section 1 "Cache": the latent cache is stored in FP8 and grows by
+# the new positions of every step.  The quantiser (nearest E4M3FN code, ties to even,
+# saturating at 448) is pinned to the format's own codes, to torch's independent E4M3FN
+# cast, and to worked ties; the append to positions and pages.
+
+def _finite_codes():
+    return np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def pin_quantiser_roundtrip(quantise):
+    """Every finite code decodes to a value that encodes back to the same code."""
+    codes = _finite_codes()
+    vals = oracle.e4m3fn_codes_to_f64(codes).astype(np.float32)
+    return np.flatnonzero(quantise(vals) != codes).tolist()
+
+
+def pin_quantiser_library(quantise, n=200_000):
+    """Against torch's float8_e4m3fn cast (round to nearest even) inside [-448, 448]:
+    random magnitudes over the whole range, every code, and every midpoint between
+    neighbouring codes (the ties)."""
+    import torch
+
+    rng = np.random.default_rng(71)
+    mags = np.exp2(rng.uniform(-12.0, np.log2(448.0), n))
+    signs = np.where(rng.random(n) < 0.5, -1.0, 1.0)
+    pos = oracle.e4m3fn_codes_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2
+    vals = np.concatenate([mags * signs, pos, -pos, mids, -mids]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return int(np.count_nonzero(quantise(vals) != ref))
+
+
+QUANTISER_WORKED = [  # (fp32 value, code): ties go to the even code; past 448 saturates
+    # (near the top the codes are 384 0x7C, 416 0x7D, 448 0x7E: 400 and 432 are ties)
+    (1.0625, 0x38), (1.1875, 0x3A), (-1.0625, 0xB8), (432.0, 0x7E), (400.0, 0x7C),
+    (447.0, 0x7E), (464.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE), (np.inf, 0x7E),
+    (-np.inf, 0xFE), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (2.0 ** -9, 0x01),
+    (0.0, 0x00), (-0.0, 0x80), (2.0 ** -6, 0x08), (15 * 2.0 ** -10, 0x08),
+]
+
+
+def pin_quantiser_worked(quantise):
+    vals = np.array([v for v, _ in QUANTISER_WORKED], dtype=np.float32)
+    want = np.array([c for _, c in QUANTISER_WORKED], dtype=np.uint8)
+    return np.flatnonzero(quantise(vals) != want).tolist()
+
+
+def test_quantiser_roundtrip_all_codes():
+    assert pin_quantiser_roundtrip(oracle.quantize_e4m3fn) == []
+
+
+def test_quantiser_matches_library_cast():
+    assert pin_quantiser_library(oracle.quantize_e4m3fn) == 0
+
+
+def test_quantiser_worked_ties_and_saturation():
+    assert pin_quantiser_worked(oracle.quantize_e4m3fn) == []
+
+
+def _append_case(kv_format, seed=81):
+    wl = wk.make_workload(None, seed=seed, batch=3, q_len=3, num_heads=2, seq_lens=[3, 64, 130],
+                          kv_format=kv_format, shuffled=True)
+    rng = np.random.default_rng(seed + 1)
+    lat = wk.to_bf16_bits(rng.standard_normal((3, 3, oracle.D_LATENT)).astype(np.float32) * 4)
+    return wl, lat
+
+
+def pin_kv_append(append_fn):
+    """The new rows land at positions L - T .. L - 1 through the block table, stored as
+    the cache format stores them (bf16 bits, or the library cast of x / scale), and no
+    other byte of the pool changes.  Returns the failures."""
+    import torch
+
+    fails = []
+    for kv_format in ("bf16", "fp8_e4m3fn"):
+        wl, lat = _append_case(kv_format)
+        scale = wl.kv_scale
+        new = append_fn(wl.pool, wl.block_table, wl.seq_lens, lat, 3, kv_format, scale, 64)
+        touched = np.zeros(wl.pool.shape[:2], dtype=bool)
+        for r, L in enumerate(wl.seq_lens):
+            for t in range(3):
+                j = int(L) - 3 + t
+                page, slot = int(wl.block_table[r][j // 64]), j % 64
+                touched[page, slot] = True
+                if kv_format == "bf16":
+                    want = lat[r, t]
+                else:
+                    x = (lat[r, t].astype(np.uint32) << 16).view(np.float32) / np.float32(scale)
+                    want = torch.from_numpy(np.clip(x, -448, 448).astype(np.float32)).to(
+                        torch.float8_e4m3fn).view(torch.uint8).numpy()
+                if not np.array_equal(new[page, slot], want):
+                    fails.append((kv_format, r, t))
+        if not np.array_equal(new[~touched], wl.pool[~touched]):
+            fails.append((kv_format, "untouched rows changed"))
+    return fails
+
+
+def test_kv_append_positions_and_storage():
+    assert pin_kv_append(oracle.kv_append) == []
+
+
+def test_kv_append_then_decode_sees_the_new_rows():
+    """Decoding after the append equals decoding a history built with the new rows."""
+    wl, lat = _append_case("fp8_e4m3fn", seed=91)
+    new = oracle.kv_append(wl.pool, wl.block_table, wl.seq_lens, lat, 3, "fp8_e4m3fn",
+                           wl.kv_scale, 64)
+    o1, l1 = oracle.decode_paged(wl.q_bits, new, "fp8_e4m3fn", wl.kv_scale, wl.block_table,
+                                 wl.seq_lens, 64, wl.softmax_scale)
+    for r, L in enumerate(wl.seq_lens):
+        rows = oracle.gather_latents(new, wl.block_table[r], int(L), 64)
+        want = np.stack([oracle.stored_row(lat[r, t], "fp8_e4m3fn", wl.kv_scale) for t in range(3)])
+        assert np.array_equal(rows[-3:], want)
+    assert np.isfinite(o1).all() and np.isfinite(l1).all()
+
+
+def test_quantiser_mutants_fail_a_pin():
+    def truncating(x32):   # toward zero instead of nearest
+        x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+        pos = oracle.e4m3fn_codes_to_f64(np.arange(0x7F, dtype=np.uint8))
+        a = np.minimum(np.abs(x), 448.0)
+        code = (np.searchsorted(pos, a, side="right") - 1).astype(np.uint8)
+        return code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+
+    def ties_away(x32):    # ties away from zero instead of to even
+        x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+        pos = oracle.e4m3fn_codes_to_f64(np.arange(0x7F, dtype=np.uint8))
+        a = np.minimum(np.abs(x), 448.0)
+        hi = np.minimum(np.searchsorted(pos, a, side="left"), 126)
+        lo = np.maximum(hi - 1, 0)
+        code = np.where(pos[hi] - a <= a - pos[lo], hi, lo).astype(np.uint8)
+        return code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+
+    def no_saturation(x32):  # past 448 becomes the NaN code
+        x = np.asarray(x32, dtype=np.float32)
+        c = oracle.quantize_e4m3fn(x)
+        return np.where(np.abs(x) > 448, c | np.uint8(0x7F), c).astype(np.uint8)
+
+    for mutant in (truncating, ties_away, no_saturation):
+        assert (pin_quantiser_roundtrip(mutant) or pin_quantiser_library(mutant, n=20_000)
+                or pin_quantiser_worked(mutant)), mutant.__name__
+
+
+def test_kv_append_mutant_fails():
+    def shifted(pool, block_table, seq_lens, lat, q_len, kv_format, scale, page_size):
+        # one position too far
+        return oracle.kv_append(pool, block_table, np.asarray(seq_lens) + 1, lat, q_len,
+                                kv_format, scale, page_size)
+    assert pin_kv_append(shifted) != []
