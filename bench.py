@@ -56,6 +56,12 @@ def parse():
     ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--q-len", type=int, default=0,
+                    help="query tokens per request (draft depth of a verification step): the "
+                         "workload's history prefix is kept and the T new tokens added to it")
+    ap.add_argument("--append", action="store_true",
+                    help="time the cache append of the step's new tokens (mla_kv_append) instead "
+                         "of the decode, alone and followed by the decode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -115,6 +121,63 @@ def cpu_baseline(wl, seconds):
     }
 
 
+def bench_append(args, wl, mb, pools, scales, dev0, kv_dtype, decode_step, nl):
+    """µs per mla_kv_append of the step's B x T new latents into one layer's pool, alone
+    and followed by that layer's decode (graph replay over the rotated pools)."""
+    import torch
+
+    B, T = wl.batch, wl.q_len
+    rng = np.random.default_rng(5)
+    lat = torch.from_numpy(rng.standard_normal((B, T, 576)).astype(np.float32)).to(torch.bfloat16).cuda()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nl):
+                fn(i)
+        reps = max(1, args.steps // nl)
+        for _ in range(max(1, args.warmup // nl)):
+            g.replay()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(args.repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            res.append(e0.elapsed_time(e1) / (reps * nl) * 1e3)
+        return float(np.median(res))
+
+    def append(i):
+        mb.kv_append(pools[i % nl], dev0["block_table"], dev0["seq_lens"], lat, kv_dtype, scales[i % nl])
+
+    def append_then_decode(i):
+        append(i)
+        decode_step(i)
+
+    us_app = timed(append)
+    us_both = timed(append_then_decode)
+    us_dec = timed(lambda i: decode_step(i))
+    elem = wk_elem(wl.kv_format)
+    moved = B * T * 576 * (2 + elem)
+    print(json.dumps({
+        "metric": "MLA cache append us per layer (the step's new latents, FP8 quantised or bf16)",
+        "value": round(us_app, 3), "unit": "us", "higher_is_better": False, "n_gpus": 1,
+        "data": "synthetic", "dtype": wl.kv_format,
+        "config": {"workload": describe(wl, 0), "new_rows": B * T},
+        "append_GBps": round(moved / (us_app * 1e-6) / 1e9, 3),
+        "append_then_decode_us": round(us_both, 3), "decode_us": round(us_dec, 3),
+        "bytes_per_append": moved,
+    }))
+
+
+def wk_elem(kv_format):
+    return 2 if kv_format == "bf16" else 1
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -131,7 +194,13 @@ def main():
         return
     mb.load(build_if_missing=False)
     torch.cuda.set_device(0)
-    wl = wk.make_workload(args.workload)
+    over = {}
+    if args.q_len:
+        spec = wk.CONFIGS[args.workload]
+        if "seq_len" not in spec:
+            sys.exit("--q-len needs a workload with one history length")
+        over = dict(q_len=args.q_len, seq_len=spec["seq_len"] - spec["q_len"] + args.q_len)
+    wl = wk.make_workload(args.workload, **over)
     splits = 0 if args.splits == "auto" else int(args.splits)
     kv_dtype = mb.MLA_BF16 if wl.kv_format == "bf16" else mb.MLA_FP8_E4M3FN
     nl = max(1, args.layers)
@@ -162,6 +231,10 @@ def main():
     def step(i, full=True):
         mb.decode_splitkv(plan, q, kvs[i % nl], ws, out=out if full else None,
                           out_dtype=mb.MLA_BF16, out_lse=lse if full else None)
+
+    if args.append:
+        bench_append(args, wl, mb, pools, scales, dev0, kv_dtype, step, nl)
+        return
 
     def timed(full, steps):
         """Average ms per call over `steps` calls (events on the launch stream)."""

@@ -158,7 +158,8 @@ void mla_plan_destroy(mla_plan* plan);
 int32_t mla_plan_num_units(const mla_plan* plan);
 int32_t mla_plan_num_parts(const mla_plan* plan);
 /* Workgroups per work unit: the 16-row blocks of the problem (q_len * ceil(num_heads/16))
- * are dealt to that many workgroups, two per workgroup when their count is even. */
+ * are dealt to that many workgroups, two per workgroup from two row blocks on (an odd
+ * count is padded with one row block that is computed and discarded). */
 int32_t mla_plan_row_groups(const mla_plan* plan);
 /*
  * Host copy of the work list, for inspection: 5 int32 per piece
@@ -206,6 +207,30 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
 mla_status mla_merge_lse(const void* part_o, int32_t part_dtype, const float* part_lse,
                          int32_t num_parts, int64_t rows, void* out, int32_t out_dtype,
                          float* out_lse, void* stream);
+
+/*
+ * Append the q_len new tokens' latents of every request to the paged cache of one layer
+ * (section 1 "Cache": one 576-value latent per cached position and layer, stored in
+ * FP8, growing by the new tokens of every step; the model side hands them over in BF16).
+ *   pool        [num_pages][page_size][576] of kv_dtype, device memory, 16-byte aligned;
+ *               written in place (only the new positions' rows)
+ *   kv_dtype    MLA_BF16: the bf16 bits are copied.  MLA_FP8_E4M3FN: each value x is
+ *               stored as the E4M3FN code nearest to fp32(x) / kv_scale (an fp32
+ *               division), ties to the even code, magnitudes past 448 saturating to
+ *               +-448, NaN to a NaN code
+ *   kv_scale    as in mla_paged_kv (finite > 0 for FP8, exactly 1 for bf16)
+ *   block_table, max_pages_per_seq, seq_lens: as in mla_paged_kv, device memory;
+ *               seq_lens[r] counts the new tokens, so token t of request r goes to
+ *               position seq_lens[r] - q_len + t
+ *   latents     bf16 [batch][q_len][576], device memory, 16-byte aligned
+ * A new position below 0, past the block-table row, or whose page id is outside
+ * [0, num_pages), is skipped on the device (nothing is written for it).  Enqueued on
+ * `stream`; a decode that reads the new positions must be ordered after it.
+ */
+mla_status mla_kv_append(void* pool, int64_t num_pages, int32_t page_size, int32_t kv_dtype,
+                         float kv_scale, const int32_t* block_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, const void* latents, int32_t batch,
+                         int32_t q_len, void* stream);
 
 /*
  * Host-side block-table check: every page a request reads (the first

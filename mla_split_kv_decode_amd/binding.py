@@ -70,6 +70,8 @@ def _signatures():
         "mla_decode_splitkv": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_size_t, P, c.c_int32,
                                          P, P]),
         "mla_merge_lse": (c.c_int, [P, c.c_int32, P, c.c_int32, c.c_int64, P, c.c_int32, P, P]),
+        "mla_kv_append": (c.c_int, [P, c.c_int64, c.c_int32, c.c_int32, c.c_float, P, c.c_int32, P, P,
+                                    c.c_int32, c.c_int32, P]),
         "mla_block_table_check": (c.c_int, [P, c.c_int32, c.c_int32, P, c.c_int32, c.c_int64]),
         "mla_page_bytes": (c.c_size_t, [c.c_int32, c.c_int32]),
         "mla_status_str": (c.c_char_p, [c.c_int]),
@@ -209,6 +211,17 @@ def decode_splitkv(plan, q, kv, ws, out=None, out_dtype=MLA_BF16, out_lse=None, 
     _check(lib.mla_decode_splitkv(plan.handle, _ptr(q), ctypes.byref(kv), _ptr(ws),
                                   ws.numel() * ws.element_size(), _ptr(out), int(out_dtype),
                                   _ptr(out_lse), _stream(stream)))
+
+
+def kv_append(pool, block_table, seq_lens, latents, kv_dtype, kv_scale=1.0, stream=None,
+              page_size=PAGE_SIZE):
+    """mla_kv_append on torch tensors: pool [num_pages][page_size][576] (written in place),
+    latents bf16 [batch][q_len][576]."""
+    lib = load()
+    batch, q_len = int(latents.shape[0]), int(latents.shape[1])
+    _check(lib.mla_kv_append(_ptr(pool), int(pool.shape[0]), int(page_size), int(kv_dtype),
+                             float(kv_scale), _ptr(block_table), int(block_table.shape[1]),
+                             _ptr(seq_lens), _ptr(latents), batch, q_len, _stream(stream)))
 
 
 def merge_lse(part_o, part_lse, out=None, out_lse=None, stream=None):

@@ -19,6 +19,9 @@ hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
                         int max_row_slots, hipStream_t stream);
 size_t partial_lds_size(bool fp8, int rbw);
+hipError_t launch_kv_append(void* pool, int64_t num_pages, bool fp8, const int32_t* block_table,
+                            int32_t max_pages, const int32_t* seq_lens, const void* latents,
+                            int32_t rows, int32_t q_len, float kv_scale, hipStream_t stream);
 }  // namespace mla
 
 using namespace mla;
@@ -185,10 +188,10 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   pl->num_cus = num_cus;
   pl->head_groups = (int32_t)head_groups;
   pl->row_blocks = (int32_t)row_blocks;
-  // two row blocks per workgroup when they pair up (every K and V^T operand read from LDS
-  // then feeds two MFMAs), else one
-  pl->rbw = row_blocks % 2 == 0 ? 2 : 1;
-  pl->row_groups = (int32_t)row_blocks / pl->rbw;
+  // two row blocks per workgroup from two on (every V^T operand read from LDS then feeds
+  // two MFMAs; an odd count gets one padding row block), else one
+  pl->rbw = row_blocks >= 2 ? 2 : 1;
+  pl->row_groups = (int32_t)((row_blocks + pl->rbw - 1) / pl->rbw);
   pl->rows = s.q_len * s.num_heads;
   pl->total_pages = total_pages;
   pl->max_req_pages = max_req_pages;
@@ -393,6 +396,31 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   }
   e = launch_merge(mp, plan->part_bf16, true, (int64_t)s.batch * plan->rows, plan->max_req_slots, st);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mla_status mla_kv_append(void* pool, int64_t num_pages, int32_t page_size, int32_t kv_dtype,
+                         float kv_scale, const int32_t* block_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, const void* latents, int32_t batch,
+                         int32_t q_len, void* stream) {
+  if (!pool || !block_table || !seq_lens || !latents) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (batch < 1 || q_len < 1 || num_pages < 1 || max_pages_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch, q_len, num_pages, max_pages_per_seq must be >= 1");
+  if ((int64_t)batch * q_len > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "batch * q_len too large");
+  if (page_size != kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (only %d)", page_size, kPage);
+  const bool fp8 = kv_dtype == MLA_FP8_E4M3FN;
+  if (!fp8 && kv_dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "kv_dtype %d", kv_dtype);
+  if (fp8) {
+    if (!(kv_scale > 0.f) || !std::isfinite(kv_scale))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "kv_scale must be finite and > 0");
+  } else if (kv_scale != 1.0f) {
+    return fail(MLA_ERR_INVALID_ARGUMENT, "kv_scale must be 1 for bf16 KV");
+  }
+  if (!aligned(pool, 16) || !aligned(latents, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "pool and latents must be 16-byte aligned, tables 4-byte");
+  hipError_t e = launch_kv_append(pool, num_pages, fp8, block_table, max_pages_per_seq, seq_lens,
+                                  latents, batch * q_len, q_len, kv_scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -296,8 +296,8 @@ struct PageCopy {
 // LDS staging area of RB x 16 rows of 576 bf16, laid out like a bf16 page tile (same chunk
 // swizzle), so one HBM read serves every wave that shares a row block.  Row i of row
 // block rb is head 16 hg + i of token t (rb = t * head_groups + hg); a padding head
-// repeats the last real head (its results are discarded).  Same operation-count rule as
-// PageCopy.
+// repeats the last real head, and a padding row block (past rb_last) the last real row
+// block (their results are discarded).  Same operation-count rule as PageCopy.
 template <int NW, int RB>
 struct QueryCopy {
   using TG = TileGeom<false>;
@@ -306,7 +306,8 @@ struct QueryCopy {
   int wave, lane;
   __device__ __forceinline__ QueryCopy(int wave_, int lane_) : wave(wave_), lane(lane_) {}
   __device__ __forceinline__ void operator()(uint32_t base, const uint16_t* q_req,
-                                             int num_heads, int head_groups, int rb0) const {
+                                             int num_heads, int head_groups, int rb0,
+                                             int rb_last) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       int k = wave + NW * j;
@@ -314,7 +315,7 @@ struct QueryCopy {
       const int s = k * 64 + lane;
       const int row = s / TG::kChunksPerRow, cs = s - row * TG::kChunksPerRow;
       const int lrb = row / kRowsPerBlock, i = row - lrb * kRowsPerBlock;
-      const int rb = rb0 + lrb;
+      const int rb = min(rb0 + lrb, rb_last);  // a padding row block repeats the last
       const int t = rb / head_groups, hg = rb - t * head_groups;
       const int head = min(hg * kRowsPerBlock + i, num_heads - 1);
       const int off = (t * num_heads + head) * TG::kRowBytes + TG::swz(row, cs) * 16;
@@ -427,7 +428,7 @@ __device__ __forceinline__ void store_partial(void* part_o, bool bf16, int64_t o
 // landed, so once the stream ends only the last page's work remains.
 //
 // Row block rb = t * head_groups + hg holds heads 16 hg .. 16 hg + 15 of query token t.
-// A problem with more than RBW row blocks runs row_groups = row blocks / RBW workgroups
+// A problem with more than RBW row blocks runs row_groups = ceil(row blocks / RBW) workgroups
 // per unit, each on the same pieces with its own row blocks.  They read the same pages:
 // the block index puts all row groups of a unit on one XCD (workgroups are dealt to the
 // eight XCDs by block index modulo 8) at about the same time, so the repeated reads of a
@@ -497,14 +498,17 @@ __device__ __forceinline__ void partial_ks(
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int u = wave & 3, kh = wave >> 2;  // sub-tile, k-half
   // this workgroup's row blocks: token, output row of this lane's head, causal lag
+  // (an odd row-block count is padded with one row block that repeats the last real one
+  // and stores nothing)
   int orow[RBW], lag[RBW];
   bool head_ok[RBW];
+  const int rb_last = args.qlen * args.hgroups - 1;
 #pragma unroll
   for (int j = 0; j < RBW; ++j) {
-    const int rb = g * RBW + j;
+    const int rb = min(g * RBW + j, rb_last);
     const int t = rb / args.hgroups, hg = rb - t * args.hgroups;
     const int head = hg * kRowsPerBlock + lrow;
-    head_ok[j] = head < args.heads;
+    head_ok[j] = head < args.heads && g * RBW + j <= rb_last;
     orow[j] = t * args.heads + head;
     lag[j] = args.causal ? args.qlen - 1 - t : 0;  // token t sees positions < L - lag
   }
@@ -541,7 +545,7 @@ __device__ __forceinline__ void partial_ks(
     // ---- queries through LDS (one HBM read per workgroup), then the first pages
     unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
     typename C::QC(wave, lane)(tiles_lds + kEarlyTiles * TG::kPageBytes, q_ptr + (int64_t)r * args.qlen * args.heads * kDLatent, args.heads,
-                               args.hgroups, g * RBW);
+                               args.hgroups, g * RBW, rb_last);
     int early = 0;
 #pragma unroll
     for (int ti = 0; ti < kEarlyTiles; ++ti) {
@@ -1126,6 +1130,53 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MergePara
     p.out_lse[orow] = inconsistent ? __builtin_nanf("") : (empty ? kNegInf : M + log2_fast(den) * kLn2);
 }
 
+// ------------------------------------------------------------------- cache append
+//
+// One workgroup per new row (request r, token t): 72 lanes take 8 of the 576 values each
+// (16 bytes of bf16).  bf16 pools get the bits; FP8 pools get the E4M3FN code of the fp32
+// quotient x / scale, converted two at a time by the gfx950 conversion instruction
+// (round to nearest even) after a clamp to +-448, which makes it saturate.
+constexpr int kAppendThreads = 128;
+
+template <bool FP8>
+__global__ __launch_bounds__(kAppendThreads) void mla_kv_append_kernel(
+    uint8_t* __restrict__ pool, int64_t num_pages, const int32_t* __restrict__ block_table,
+    int32_t max_pages, const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ latents,
+    int32_t q_len, float kv_scale) {
+  // every argument in one batch of scalar loads (the compiler would fetch them lazily,
+  // one round trip each), then the latents: their load overlaps the length -> page-id chain
+  asm volatile("" ::"s"(pool), "s"(num_pages), "s"(block_table), "s"(max_pages), "s"(seq_lens),
+               "s"(latents), "s"(q_len), "s"(kv_scale));
+  const int i = threadIdx.x;
+  if (i >= kDLatent / 8) return;
+  const int r = blockIdx.x / q_len, t = blockIdx.x - r * q_len;
+  const bf16x8 x = *(const bf16x8*)(latents + (int64_t)blockIdx.x * kDLatent + 8 * i);
+  asm volatile("" ::: "memory");  // keeps the latent load ahead of the chain below
+  const int j = seq_lens[r] - q_len + t;  // the new position
+  // the table entry is read at a clamped (in-bounds) index whatever j is, so that no
+  // branch separates the loads; the checks only decide the store
+  const int pg = min(max(j, 0) / kPage, max_pages - 1);
+  const int32_t id = block_table[(int64_t)r * max_pages + pg];
+  if (j < 0 || j / kPage >= max_pages || id < 0 || id >= num_pages) return;
+  const int64_t row = (int64_t)id * kPage + j % kPage;
+  if constexpr (!FP8) {
+    *(bf16x8*)(pool + (row * kDLatent + 8 * i) * 2) = x;
+  } else {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float q = (float)x[k] / kv_scale;  // correctly rounded fp32 division
+      v[k] = q != q ? q : fminf(fmaxf(q, -448.f), 448.f);
+    }
+    i32x2 codes;
+    codes[0] = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    codes[0] = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], codes[0], true);
+    codes[1] = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    codes[1] = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], codes[1], true);
+    *(i32x2*)(pool + row * kDLatent + 8 * i) = codes;
+  }
+}
+
 // ------------------------------------------------------------------- kernels
 
 constexpr int kPartialThreads = 512;
@@ -1165,10 +1216,26 @@ size_t partial_lds_size(bool fp8, int rbw) {
 }
 
 hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream) {
-  if (p.row_groups < 1 || p.rbw * p.row_groups != p.q_len * p.head_groups) return hipErrorInvalidValue;
+  const int rbs = p.q_len * p.head_groups;
+  if (p.row_groups < 1 || p.rbw * p.row_groups < rbs || p.rbw * (p.row_groups - 1) >= rbs)
+    return hipErrorInvalidValue;
   if (p.rbw == 1) return fp8 ? launch_partial_t<true, 1>(p, stream) : launch_partial_t<false, 1>(p, stream);
   if (p.rbw == 2) return fp8 ? launch_partial_t<true, 2>(p, stream) : launch_partial_t<false, 2>(p, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_append(void* pool, int64_t num_pages, bool fp8, const int32_t* block_table,
+                            int32_t max_pages, const int32_t* seq_lens, const void* latents,
+                            int32_t rows, int32_t q_len, float kv_scale, hipStream_t stream) {
+  if (fp8)
+    hipLaunchKernelGGL((mla_kv_append_kernel<true>), dim3(rows), dim3(kAppendThreads), 0, stream,
+                       (uint8_t*)pool, num_pages, block_table, max_pages, seq_lens,
+                       (const uint16_t*)latents, q_len, kv_scale);
+  else
+    hipLaunchKernelGGL((mla_kv_append_kernel<false>), dim3(rows), dim3(kAppendThreads), 0, stream,
+                       (uint8_t*)pool, num_pages, block_table, max_pages, seq_lens,
+                       (const uint16_t*)latents, q_len, kv_scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,

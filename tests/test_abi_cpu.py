@@ -107,6 +107,34 @@ def _fake(addr=1 << 20):
     return ctypes.c_void_p(addr)
 
 
+def test_kv_append_argument_checks_enqueue_nothing():
+    """Every failing check of mla_kv_append returns before any device call."""
+    lib = mb.load()
+    E, U = mb.MLA_ERR_INVALID_ARGUMENT, mb.MLA_ERR_UNSUPPORTED
+
+    def call(pool=_fake(1 << 22), npages=16, page=64, dt=mb.MLA_FP8_E4M3FN, scale=0.5,
+             bt=_fake(1 << 21), maxp=16, sl=_fake(1 << 23), lat=_fake(1 << 24), batch=2, q_len=1):
+        return lib.mla_kv_append(pool, npages, page, dt, scale, bt, maxp, sl, lat, batch, q_len, None)
+
+    assert call(pool=None) == E
+    assert call(bt=None) == E
+    assert call(sl=None) == E
+    assert call(lat=None) == E
+    assert call(batch=0) == E
+    assert call(q_len=0) == E
+    assert call(npages=0) == E
+    assert call(maxp=0) == E
+    assert call(page=32) == U
+    assert call(dt=mb.MLA_FP32) == U
+    assert call(scale=0.0) == E
+    assert call(scale=float("inf")) == E
+    assert call(dt=mb.MLA_BF16, scale=0.5) == E
+    assert call(pool=_fake((1 << 22) + 8)) == E
+    assert call(lat=_fake((1 << 24) + 4)) == E
+    assert call(sl=_fake((1 << 23) + 2)) == E
+    assert call(batch=1 << 20, q_len=1 << 12) == U
+
+
 def test_decode_argument_checks_enqueue_nothing():
     """Every failing check returns before any device call (so this runs on a CPU)."""
     lib = mb.load()
@@ -175,7 +203,7 @@ def check_plan(seq_lens, q_len=1, heads=16, splits=0, cus=256, dtype=mb.MLA_BF16
     assert work[:, 4].min() >= 0 and work[:, 4].max() < S
     assert set(work[:, 0]) <= set(range(W))
     rb = q_len * -(-heads // 16)
-    G = rb // 2 if rb % 2 == 0 else rb  # row blocks go two to a workgroup when they pair up
+    G = 1 if rb == 1 else -(-rb // 2)  # row blocks go two to a workgroup (odd: one padding)
     assert plan.row_groups == G
     if splits == 0:
         P = sum(pages)

@@ -487,3 +487,91 @@ def test_large_batch_device_lengths_path():
     mb.decode_splitkv(plan, dev["q"], kv, ws, out=out, out_lse=lse)
     torch.cuda.synchronize()
     assert torch.isnan(lse).all()
+
+
+# ------------------------------------------------------------ cache append
+
+def _append_inputs(kv_format, seed, batch, q_len, seq_lens, special=False):
+    import torch
+
+    wl = wk.make_workload(None, seed=seed, batch=batch, q_len=q_len, num_heads=16,
+                          seq_lens=seq_lens, kv_format=kv_format, shuffled=True)
+    rng = np.random.default_rng(seed + 1)
+    x = rng.standard_normal((batch, q_len, oracle.D_LATENT)).astype(np.float32) * 3
+    scale = float(wl.kv_scale)
+    if special:  # ties, saturation, signed zeros and subnormal codes after x / scale
+        if kv_format != "bf16":  # a power of two keeps x * scale and x / scale exact
+            scale = float(2.0 ** np.round(np.log2(scale)))
+        s = scale
+        vals = np.array([1.0625, 1.1875, -1.0625, 432.0, 400.0, 447.0, 464.0, 1e6, -1e6, 2.0 ** -10,
+                         3 * 2.0 ** -10, 2.0 ** -9, 0.0, -0.0, 2.0 ** -6, 15 * 2.0 ** -10, np.inf, -np.inf],
+                        dtype=np.float64)
+        x[0, 0, :len(vals)] = (vals * s).astype(np.float32)
+    lat = wk.to_bf16_bits(x)
+    dev = wk.to_device(wl)
+    lat_dev = torch.from_numpy(lat.view(np.int16)).cuda().view(torch.bfloat16)
+    return wl, lat, dev, lat_dev, scale
+
+
+def _pool_bytes(pool_tensor):
+    import torch
+
+    t = pool_tensor.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint8)
+
+
+@pytest.mark.parametrize("kv_format", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_kv_append_bit_exact(kv_format, q_len):
+    """Every byte of the pool after the append equals the oracle's (new rows written,
+    nothing else touched), including ties, saturation and signed zeros."""
+    import torch
+
+    wl, lat, dev, lat_dev, scale = _append_inputs(kv_format, 501 + q_len, 3, q_len,
+                                                  [q_len, 64 + q_len, 300], special=True)
+    kvd = kv_dtype_of(wl)
+    mb.kv_append(dev["pool"], dev["block_table"], dev["seq_lens"], lat_dev, kvd, scale)
+    torch.cuda.synchronize()
+    got = _pool_bytes(dev["pool"]).reshape(wl.pool.shape)
+    want = oracle.kv_append(wl.pool, wl.block_table, wl.seq_lens, lat, q_len, kv_format,
+                            scale, wl.page_size)
+    bad = np.argwhere(got != want)
+    print(f"[append] {kv_format} T={q_len}: {len(bad)} differing bytes of {got.size}", flush=True)
+    assert len(bad) == 0, bad[:8]
+
+
+def test_kv_append_skips_invalid_positions():
+    """A device length below q_len, and a page id outside the pool, write nothing."""
+    import torch
+
+    wl, lat, dev, lat_dev, _ = _append_inputs("fp8_e4m3fn", 601, 3, 2, [100, 200, 50])
+    sl = dev["seq_lens"].clone()
+    sl[0] = 1  # below q_len: request 0 has no valid new positions 0 - 1 .. 0
+    bt = dev["block_table"].clone()
+    bt[2, (50 - 2) // 64] = 10 ** 6  # request 2's new rows point outside the pool
+    mb.kv_append(dev["pool"], bt, sl, lat_dev, mb.MLA_FP8_E4M3FN, dev["kv_scale"])
+    torch.cuda.synchronize()
+    got = _pool_bytes(dev["pool"]).reshape(wl.pool.shape)
+    # only request 1 is written; position -1 of request 0 is skipped, position 0 written
+    want = oracle.kv_append(wl.pool, wl.block_table[1:2], wl.seq_lens[1:2], lat[1:2], 2,
+                            "fp8_e4m3fn", wl.kv_scale, 64)
+    p0 = int(wl.block_table[0][0])
+    want[p0, 0] = oracle.stored_row(lat[0, 1], "fp8_e4m3fn", wl.kv_scale)
+    assert np.array_equal(got, want)
+
+
+def test_append_then_decode():
+    """Append the new tokens of a verification step, then decode: matches the oracle on
+    the appended pool (the path a serving step takes: write the drafts, verify them)."""
+    import torch
+
+    wl, lat, dev, lat_dev, _ = _append_inputs("fp8_e4m3fn", 701, 2, 3, [500, 130])
+    mb.kv_append(dev["pool"], dev["block_table"], dev["seq_lens"], lat_dev, mb.MLA_FP8_E4M3FN,
+                 dev["kv_scale"])
+    new_pool = oracle.kv_append(wl.pool, wl.block_table, wl.seq_lens, lat, 3, "fp8_e4m3fn",
+                                wl.kv_scale, 64)
+    o, l = run_gpu(wl, num_splits=0, dev=dev)
+    o_ref, l_ref = run_oracle(wl, pool=new_pool)
+    compare(wl, o, l, o_ref, l_ref, "after append")
