@@ -528,12 +528,12 @@ __device__ __forceinline__ void partial_ks(
     const int32_t* trow = block_table + (int64_t)r * args.maxp;
     const int n = pe - pb;
     bool bad = false;
-    // page i of the piece into tile i % kTiles; an id outside the pool is never
-    // dereferenced (page 0 is copied instead, the piece becomes NaN)
-    auto issue = [&](int i) {
+    // page i of the piece, whose block-table entry is id, into tile i % kTiles; an id
+    // outside the pool is never dereferenced (page 0 is copied instead, the piece becomes NaN)
+    auto page_id = [&](int i) -> int32_t { return i < n ? trow[pb + i] : 0; };
+    auto issue_id = [&](int i, int32_t id) {
       if (i >= n) return;
       const int lp = pb + i;
-      int32_t id = trow[lp];
       if ((uint64_t)(int64_t)id >= (uint64_t)args.npages) {
         bad = true;
         id = 0;
@@ -541,6 +541,7 @@ __device__ __forceinline__ void partial_ks(
       copy(tiles_lds + (i % kTiles) * TG::kPageBytes, pool + (int64_t)id * TG::kPageBytes,
            min(kPage, L - lp * kPage));
     };
+    auto issue = [&](int i) { issue_id(i, page_id(i)); };
 
     // ---- queries through LDS (one HBM read per workgroup), then the first pages
     unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
@@ -581,10 +582,25 @@ __device__ __forceinline__ void partial_ks(
       for (int ct = 0; ct < CT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // Multi-row and FP8 kernels: the copy of page i + kTiles - 1 goes out as soon as page i
+    // has landed everywhere.  The barrier that says so also says every wave is done with
+    // page i - 1, whose tile it reuses, so no barrier of its own is needed, and its
+    // block-table entry is read one page earlier, off the critical path.  The one-row-block
+    // bf16 kernel (mostly a few pages per piece) measured faster with the copy of page
+    // i + kTiles issued after a barrier at the end of page i.
+    constexpr bool kTopIssue = FP8 || RBW == 2;
+    int32_t next_id = kTopIssue ? page_id(kTiles) : 0;
     for (int i = 0; i < n; ++i) {
-      // pages i+1 .. i+kTiles-1 were issued after page i: let them fly
-      wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
+      // the pages issued after page i may stay in flight (top issue: kTiles - 1 of them
+      // before the loop's first copy, kTiles - 2 afterwards)
+      if constexpr (kTopIssue)
+        wait_pages<kPer, kTiles - 1>(min(n, i == 0 ? kTiles : i + kTiles - 1) - (i + 1));
+      else
+        wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
       barrier_lds();  // every wave's copies of page i have landed
+      if constexpr (kTopIssue) {
+        if (i > 0) issue_id(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
+      }
       const unsigned char* tile = tiles + (i % kTiles) * TG::kPageBytes;
       const int lp = pb + i;
 
@@ -786,10 +802,12 @@ __device__ __forceinline__ void partial_ks(
             acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[j][ct], 0, 0, 0);
         }
       }
-
-      // the next copy into this tile waits until every wave is done with it
-      if (i + kTiles < n) {
-        barrier_lds();
+      if constexpr (kTopIssue) {
+        // (a scalar load here lands under the MFMAs; earlier, it would hold up the first
+        // wait for the page's LDS reads, which shares its counter)
+        if (i > 0) next_id = page_id(i + kTiles);
+      } else if (i + kTiles < n) {
+        barrier_lds();  // every wave is done with this tile
         issue(i + kTiles);
       }
     }
