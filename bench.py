@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--append", action="store_true",
                     help="time the cache append of the step's new tokens (mla_kv_append) instead "
                          "of the decode, alone and followed by the decode")
+    ap.add_argument("--fp8-qk", action="store_true",
+                    help="q.k on the FP8 matrix cores (FP8 pool, two or more 16-row blocks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -218,7 +220,7 @@ def main():
     t_plan = time.perf_counter()
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
                    causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype,
-                   partials_bf16=args.partial == "bf16")
+                   partials_bf16=args.partial == "bf16", fp8_qk=args.fp8_qk)
     t_plan = time.perf_counter() - t_plan
     ws = mb.workspace(plan)
     B, T, H = wl.batch, wl.q_len, wl.num_heads
@@ -286,7 +288,7 @@ def main():
     part_gbs = kv_b / (ms_part * 1e-3) / 1e9
     flops = wk.attention_flops(wl.seq_lens, wl.q_len, wl.num_heads, wl.causal)
     traffic = None
-    tr = TRAFFIC.get((wl.name, splits, args.partial, mb.version()))
+    tr = None if args.fp8_qk else TRAFFIC.get((wl.name, splits, args.partial, mb.version()))
     if tr:
         traffic = int(1024 * (tr["fetch_kib"] * tr["fetch_factor"] + tr["write_kib"] * tr["write_factor"]))
     res = {
@@ -307,6 +309,7 @@ def main():
             "batch": B, "q_len": T, "num_heads": H, "seq_len": int(wl.seq_lens.max()),
             "kv_dtype": wl.kv_format, "splits": "auto" if splits == 0 else splits,
             "layers_rotated": nl, "launch": args.mode, "partials": args.partial,
+            "qk": "fp8" if args.fp8_qk else "bf16",
         },
         "us_per_layer_step": round(ms * 1e3, 3),
         "pct_of_8TBs": round(100 * gbs / HBM_PEAK_GBS, 2),

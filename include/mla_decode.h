@@ -162,6 +162,19 @@ int32_t mla_plan_num_parts(const mla_plan* plan);
  * count is padded with one row block that is computed and discarded). */
 int32_t mla_plan_row_groups(const mla_plan* plan);
 /*
+ * Optional FP8 matrix-core form of q.k for an FP8 pool (Kimi K3 on MI355X, section 1
+ * "Cache": the latents are stored in FP8; the same section's DCP8 paragraph: one shard
+ * holds all 96 heads).  enable = 1: the partial stage feeds the pool's E4M3FN codes to
+ * the FP8 matrix cores as they are, and each query row as two E4M3FN vectors hi + lo
+ * after scaling the row by a power of two (hi + lo equals every bf16 query element
+ * times that power exactly, except elements below 2^-10 of the row's largest magnitude,
+ * which keep an error below 2^-17 of it).  The value side is unchanged.  Off by default.
+ * Needs kv_dtype = MLA_FP8_E4M3FN and q_len * ceil(num_heads/16) >= 2; otherwise
+ * MLA_ERR_UNSUPPORTED (the plan is left unchanged).  enable must be 0 or 1
+ * (MLA_ERR_INVALID_ARGUMENT).
+ */
+mla_status mla_plan_set_fp8_qk(mla_plan* plan, int32_t enable);
+/*
  * Host copy of the work list, for inspection: 5 int32 per piece
  * (workgroup, request, first page, end page (exclusive), partial slot), in workgroup
  * order.  Writes at most `capacity` pieces; returns the number of pieces, or -1 on a

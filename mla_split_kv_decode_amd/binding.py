@@ -66,6 +66,7 @@ def _signatures():
         "mla_plan_num_units": (c.c_int32, [P]),
         "mla_plan_num_parts": (c.c_int32, [P]),
         "mla_plan_row_groups": (c.c_int32, [P]),
+        "mla_plan_set_fp8_qk": (c.c_int, [P, c.c_int32]),
         "mla_plan_get_work": (c.c_int32, [P, P, c.c_int32]),
         "mla_decode_splitkv": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_size_t, P, c.c_int32,
                                          P, P]),
@@ -144,7 +145,7 @@ class Plan:
 
     def __init__(self, batch, q_len, num_heads, seq_lens_host, softmax_scale, causal=True,
                  num_splits=0, kv_dtype=MLA_BF16, num_cus=0, page_size=PAGE_SIZE,
-                 partials_bf16=False):
+                 partials_bf16=False, fp8_qk=False):
         lib = load()
         self.shape = MlaDecodeShape(int(batch), int(q_len), int(num_heads), float(softmax_scale),
                                     int(bool(causal)), int(num_splits), int(bool(partials_bf16)))
@@ -158,6 +159,8 @@ class Plan:
         self.workspace_bytes = ws.value
         self.kv_dtype = kv_dtype
         self.batch, self.q_len, self.num_heads = int(batch), int(q_len), int(num_heads)
+        if fp8_qk:
+            self.set_fp8_qk(True)
 
     @property
     def handle(self):
@@ -174,6 +177,10 @@ class Plan:
     @property
     def row_groups(self):
         return load().mla_plan_row_groups(self._h)
+
+    def set_fp8_qk(self, enable):
+        """q.k on the FP8 matrix cores (FP8 pool, two or more 16-row blocks)."""
+        _check(load().mla_plan_set_fp8_qk(self._h, int(bool(enable))))
 
     def work(self):
         """Work list as int32 [n][5]: (workgroup, request, first page, end page, slot)."""

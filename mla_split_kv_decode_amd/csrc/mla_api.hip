@@ -15,7 +15,7 @@
 #include "mla_internal.h"
 
 namespace mla {
-hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_partial(const PartialParams& p, bool fp8, bool fp8_qk, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
                         int max_row_slots, hipStream_t stream);
 size_t partial_lds_size(bool fp8, int rbw);
@@ -41,6 +41,7 @@ struct mla_plan {
   int32_t num_splits;    // S (SPLIT_FIXED)
   int32_t num_slots;     // partial answers the workspace holds
   int32_t part_bf16;     // partial O element type
+  int32_t fp8_qk;        // QK^T on the FP8 matrix cores (mla_plan_set_fp8_qk)
   int64_t total_pages;
   int32_t max_req_pages;  // largest ceil(seq_len / page) of a request
   int32_t max_req_slots;  // most partial answers of one request
@@ -98,7 +99,7 @@ int wg_per_cu(bool fp8, int rbw) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.5.0 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.0 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -260,6 +261,16 @@ int32_t mla_plan_num_parts(const mla_plan* plan) { return plan ? plan->num_slots
 
 int32_t mla_plan_row_groups(const mla_plan* plan) { return plan ? plan->row_groups : -1; }
 
+mla_status mla_plan_set_fp8_qk(mla_plan* plan, int32_t enable) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "null plan");
+  if (enable != 0 && enable != 1) return fail(MLA_ERR_INVALID_ARGUMENT, "enable must be 0 or 1");
+  if (enable && (plan->kv_dtype != MLA_FP8_E4M3FN || plan->rbw != 2))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "FP8 QK^T needs an FP8 pool and q_len * ceil(num_heads/16) >= 2 (two row blocks per workgroup)");
+  plan->fp8_qk = enable;
+  return ok();
+}
+
 int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity) {
   if (!plan || capacity < 0 || (capacity > 0 && !out)) return -1;
   int32_t n = 0;
@@ -367,7 +378,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   fill_plan_args(*plan, &pp.plan);
   if (!out && !out_lse) {
     if (plan->num_wg > 0) {
-      hipError_t e = launch_partial(pp, fp8, st);
+      hipError_t e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);
       if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
     }
     return ok();
@@ -391,7 +402,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   mp.plan = pp.plan;
   hipError_t e = hipSuccess;
   if (plan->num_wg > 0) {
-    e = launch_partial(pp, fp8, st);
+    e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);
     if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
   }
   e = launch_merge(mp, plan->part_bf16, true, (int64_t)s.batch * plan->rows, plan->max_req_slots, st);

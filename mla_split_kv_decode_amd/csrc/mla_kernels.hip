@@ -166,6 +166,32 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 raw) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Eight bf16 values (the bits of q) times the power of two sc, |q sc| < 256, as two E4M3FN
+// code vectors with hi + lo = q sc: hi is q sc rounded to nearest (even), lo the remainder
+// (exact in fp32) rounded again.  A bf16 value has eight significant bits and hi keeps the
+// top four, so the remainder is an integer multiple of q's last place of at most half of
+// hi's, with at most four significant bits: lo is exact unless it falls below the E4M3FN
+// normal range, i.e. hi + lo = q sc exactly for |q sc| >= 1/4 and to within 2^-10 below.
+__device__ __forceinline__ void split_fp8x8(i32x4 q, float sc, i32x2& hi, i32x2& lo) {
+  const bf16x8 v = __builtin_bit_cast(bf16x8, q);
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e] * sc;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w], x[4 * w + 1], 0, false);
+    h = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2], x[4 * w + 3], h, true);
+    const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+    const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w] - b0[0], x[4 * w + 1] - b0[1], 0, false);
+    l = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2] - b1[0], x[4 * w + 3] - b1[1], l, true);
+    hi[w] = h;
+    lo[w] = l;
+  }
+}
+
 template <bool FP8>
 struct TileGeom {
   static constexpr int kElem = FP8 ? 1 : 2;
@@ -473,7 +499,7 @@ __device__ __forceinline__ bool unit_of_block(int nwg, int rgroups, int64_t& w, 
   return w < nwg;
 }
 
-template <bool FP8, int RBW, bool RS>
+template <bool FP8, int RBW, bool RS, bool F8QK>
 __device__ __forceinline__ void partial_ks(
     const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -486,6 +512,12 @@ __device__ __forceinline__ void partial_ks(
   // every wave shares the softmax work
   static_assert(!RS || RBW == 2, "row split needs two row blocks");
   constexpr int KQ = RS ? 2 * KS : KS;  // k-steps of queries a wave holds
+  // F8QK (FP8 pool, row split, on request): QK^T on the FP8 matrix cores, the pool's codes
+  // entering as they are and the queries as split-precision E4M3FN pairs; four 32-column
+  // k-steps per 128-deep product, the last two k-steps sharing one product (hi and lo side
+  // by side).  Only the scores' rounding changes (hi + lo reproduces each bf16 query
+  // element, see split_fp8x8); PV^T stays on bf16.
+  static_assert(!F8QK || (FP8 && RS && KQ == 18), "FP8 QK^T needs the FP8 row split");
   constexpr int NQ = RS ? 1 : RBW;      // row blocks whose queries a wave holds
   constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
   const HotArgs args(p);
@@ -571,6 +603,39 @@ __device__ __forceinline__ void partial_ks(
 #pragma unroll
     for (int ti = kEarlyTiles; ti < kTiles; ++ti) issue(ti);
 
+    // F8QK: each query row times a power of two 2^a that brings its largest magnitude into
+    // [128, 256), split into hi + lo; the scores then come out times 2^a, which the row's
+    // score scale takes back
+    i32x8 q8h[4], q8l[4], q8t;
+    float rsc = args.sscale;  // score scale of this lane's query row
+    if constexpr (F8QK) {
+      float amax = 0.f;
+#pragma unroll
+      for (int t = 0; t < KQ; ++t) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, qf[0][t]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+      }
+      amax = max_over_rows(amax);  // the four lanes of this row
+      const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 126;  // amax in [2^(ex-1), 2^ex)
+      const int a = amax > 0.f ? min(max(8 - ex, -100), 100) : 0;
+      const float sc = __uint_as_float((uint32_t)(127 + a) << 23);
+      rsc = args.sscale * __uint_as_float((uint32_t)(127 - a) << 23);
+      i32x2 h[KQ], l[KQ];
+#pragma unroll
+      for (int t = 0; t < KQ; ++t) split_fp8x8(qf[0][t], sc, h[t], l[t]);
+      // block b holds k-steps 4b, 4b+2, 4b+1, 4b+3 in that order, the order in which the
+      // paired LDS reads deliver the key codes
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        q8h[b] = i32x8{h[4 * b][0], h[4 * b][1], h[4 * b + 2][0], h[4 * b + 2][1],
+                       h[4 * b + 1][0], h[4 * b + 1][1], h[4 * b + 3][0], h[4 * b + 3][1]};
+        q8l[b] = i32x8{l[4 * b][0], l[4 * b][1], l[4 * b + 2][0], l[4 * b + 2][1],
+                       l[4 * b + 1][0], l[4 * b + 1][1], l[4 * b + 3][0], l[4 * b + 3][1]};
+      }
+      q8t = i32x8{h[16][0], h[16][1], h[17][0], h[17][1], l[16][0], l[16][1], l[17][0], l[17][1]};
+    }
+
     float m[RBW], lsum[RBW];  // running row max (log2 units, the same in every wave) and
     f32x4 acc[RBW][CT];       // this lane's share of the denominator (k-half 0 waves; RS:
                               // lsum[0], of the wave's own row block)
@@ -609,18 +674,33 @@ __device__ __forceinline__ void partial_ks(
       // softmax, so these transposing reads run under the MFMAs and the exchanges)
       const unsigned char* kt = tile + u * 16 * TG::kRowBytes;
       bf16x8 kf[KQ];
+      i32x2 kr[KQ];  // F8QK: the codes as they are
 #pragma unroll
       for (int s = 0; s < KQ; ++s) {
         const int kk = RS ? s : kh * KS + s;
         const unsigned char* ka =
             kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1) + OperandAddr<FP8>::kstep(kk);
-        if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
+        if constexpr (F8QK) kr[s] = *(const i32x2*)ka;
+        else if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
         else kf[s] = *(const bf16x8*)ka;
       }
       f32x4 sp[RBW];
 #pragma unroll
       for (int j = 0; j < RBW; ++j) sp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (RS) {
+      if constexpr (F8QK) {
+        // the key codes sit at the same bytes of each operand as the query elements of
+        // their columns; hi and lo accumulate apart (two independent chains)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const i32x8 k8 = i32x8{kr[4 * b][0], kr[4 * b][1], kr[4 * b + 2][0], kr[4 * b + 2][1],
+                                 kr[4 * b + 1][0], kr[4 * b + 1][1], kr[4 * b + 3][0], kr[4 * b + 3][1]};
+          sp[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8h[b], sp[0], 0, 0, 0, 0, 0, 0);
+          sp[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8l[b], sp[1], 0, 0, 0, 0, 0, 0);
+        }
+        const i32x8 k8 = i32x8{kr[16][0], kr[16][1], kr[17][0], kr[17][1], kr[16][0], kr[16][1], kr[17][0], kr[17][1]};
+        sp[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8t, sp[0], 0, 0, 0, 0, 0, 0);
+        sp[0] += sp[1];
+      } else if constexpr (RS) {
         // two accumulators (even and odd k-steps) halve the dependent MFMA chain
 #pragma unroll
         for (int s = 0; s < KQ; ++s)
@@ -719,7 +799,7 @@ __device__ __forceinline__ void partial_ks(
         }
         float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
         mx = max_over_rows(mx);
-        if (lgrp == 0) sm.red[kh][u * 16 + lrow] = mx * args.sscale;
+        if (lgrp == 0) sm.red[kh][u * 16 + lrow] = mx * rsc;
       } else if (kh == 0) {
         const bool whole = (lp + 1) * kPage <= L - lag_max;
 #pragma unroll
@@ -771,7 +851,7 @@ __device__ __forceinline__ void partial_ks(
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sv[0][e] = exp2_fast(fmaf(sv[0][e], args.sscale, -msub));
+          sv[0][e] = exp2_fast(fmaf(sv[0][e], rsc, -msub));
           ps += sv[0][e];
         }
         lsum[0] = fmaf(lsum[0], kh ? alpha[RBW - 1] : alpha[0], ps);
@@ -1202,23 +1282,23 @@ static_assert(KSplitCfg<false, 1>::NW * 64 == kPartialThreads, "workgroup size")
 
 // Eight waves, two per SIMD; the page tiles cap residency at one workgroup per compute
 // unit, so each wave may hold up to 256 registers.
-template <bool FP8, int RBW>
+template <bool FP8, int RBW, bool F8QK>
 __global__ __launch_bounds__(kPartialThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     void* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ KSplitSmem<FP8, RBW> sm;
-  partial_ks<FP8, RBW, RBW == 2>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+  partial_ks<FP8, RBW, RBW == 2, F8QK>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
 // ------------------------------------------------------------------ launchers
 
 namespace {
 
-template <bool FP8, int RBW>
+template <bool FP8, int RBW, bool F8QK = false>
 hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW>), dim3(partial_grid(p.num_wg, p.row_groups)),
+  hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK>), dim3(partial_grid(p.num_wg, p.row_groups)),
                      dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
                      p.seq_lens, p.part_o, p.part_lse);
   return hipGetLastError();
@@ -1233,10 +1313,14 @@ size_t partial_lds_size(bool fp8, int rbw) {
   return 0;
 }
 
-hipError_t launch_partial(const PartialParams& p, bool fp8, hipStream_t stream) {
+hipError_t launch_partial(const PartialParams& p, bool fp8, bool fp8_qk, hipStream_t stream) {
   const int rbs = p.q_len * p.head_groups;
   if (p.row_groups < 1 || p.rbw * p.row_groups < rbs || p.rbw * (p.row_groups - 1) >= rbs)
     return hipErrorInvalidValue;
+  if (fp8_qk) {  // only the FP8 row split has the FP8 QK^T form
+    if (!fp8 || p.rbw != 2) return hipErrorInvalidValue;
+    return launch_partial_t<true, 2, true>(p, stream);
+  }
   if (p.rbw == 1) return fp8 ? launch_partial_t<true, 1>(p, stream) : launch_partial_t<false, 1>(p, stream);
   if (p.rbw == 2) return fp8 ? launch_partial_t<true, 2>(p, stream) : launch_partial_t<false, 2>(p, stream);
   return hipErrorInvalidValue;

@@ -107,6 +107,26 @@ def _fake(addr=1 << 20):
     return ctypes.c_void_p(addr)
 
 
+@pytest.mark.parametrize("dtype,q_len,heads,want", [
+    (mb.MLA_FP8_E4M3FN, 1, 96, mb.MLA_OK),    # six row blocks: the FP8 row split
+    (mb.MLA_FP8_E4M3FN, 4, 16, mb.MLA_OK),    # four row blocks
+    (mb.MLA_FP8_E4M3FN, 1, 32, mb.MLA_OK),    # two
+    (mb.MLA_FP8_E4M3FN, 1, 16, mb.MLA_ERR_UNSUPPORTED),  # one row block: no row split
+    (mb.MLA_FP8_E4M3FN, 1, 12, mb.MLA_ERR_UNSUPPORTED),
+    (mb.MLA_BF16, 1, 96, mb.MLA_ERR_UNSUPPORTED),        # no FP8 codes to feed
+])
+def test_fp8_qk_option_rules(dtype, q_len, heads, want):
+    lib = mb.load()
+    plan = mb.Plan(1, q_len, heads, [1000], TAU, kv_dtype=dtype, num_cus=256)
+    assert lib.mla_plan_set_fp8_qk(plan.handle, 1) == want
+    assert lib.mla_plan_set_fp8_qk(plan.handle, 0) == mb.MLA_OK  # off is always allowed
+    assert lib.mla_plan_set_fp8_qk(plan.handle, 2) == mb.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_plan_set_fp8_qk(None, 0) == mb.MLA_ERR_INVALID_ARGUMENT
+    if want != mb.MLA_OK:
+        with pytest.raises(mb.MlaError):
+            mb.Plan(1, q_len, heads, [1000], TAU, kv_dtype=dtype, num_cus=256, fp8_qk=True)
+
+
 def test_kv_append_argument_checks_enqueue_nothing():
     """Every failing check of mla_kv_append returns before any device call."""
     lib = mb.load()

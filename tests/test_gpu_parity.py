@@ -34,7 +34,7 @@ def kv_dtype_of(wl):
 
 
 def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, heads=None,
-            block_table=None, pool=None, canary=False, partial="fp32"):
+            block_table=None, pool=None, canary=False, partial="fp32", fp8_qk=False):
     """Decode a workload on the GPU; returns (O fp64 [B][T][H][512], LSE fp64 [B][T][H])."""
     import torch
 
@@ -44,7 +44,7 @@ def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, head
     splits = wl.num_splits if num_splits is None else num_splits
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
                    causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype_of(wl),
-                   partials_bf16=partial == "bf16")
+                   partials_bf16=partial == "bf16", fp8_qk=fp8_qk)
     ws = mb.workspace(plan)
     B, T, H = wl.batch, wl.q_len, wl.num_heads
     tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
@@ -202,6 +202,73 @@ def test_dcp_fp8_shard_sampled(partial):
     req = [0, 3, 7]
     o_ref, l_ref = run_oracle(wl, requests=req, heads=heads)
     compare(wl, o[req][:, :, heads], l[req][:, :, heads], o_ref, l_ref, "shard, sampled")
+
+
+# ------------------------------------------------------------ FP8 matrix-core q.k (opt-in)
+#
+# The pool's E4M3FN codes enter the FP8 matrix cores as they are, each query row as
+# hi + lo E4M3FN after a power-of-two row scale.  Same gates as the default path; and
+# since hi + lo reproduces the bf16 query elements (all but the smallest exactly), the
+# two paths agree far inside the gates.
+
+F8QK_CASES = [c for c in SMALL if c[5] == "fp8_e4m3fn" and c[1] * -(-c[2] // 16) >= 2]
+
+
+@pytest.mark.parametrize("case", F8QK_CASES,
+                         ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}L{'-'.join(map(str, c[3]))}s{c[4]}")
+def test_fp8_qk_small_shapes(case):
+    B, T, H, seq_lens, splits, kv = case
+    wl = wk.make_workload(None, seed=101 + len(seq_lens) * 7 + T, batch=B, q_len=T, num_heads=H,
+                          seq_lens=seq_lens, kv_format=kv, shuffled=True, num_splits=splits)
+    check_full(wl, canary=True, fp8_qk=True)
+
+
+def test_fp8_qk_dcp_shard_sampled():
+    wl = wk.make_workload("dcp_fp8")
+    o, l = run_gpu(wl, fp8_qk=True)
+    heads = [0, 11, 12, 47, 95]
+    req = [0, 3, 7]
+    o_ref, l_ref = run_oracle(wl, requests=req, heads=heads)
+    compare(wl, o[req][:, :, heads], l[req][:, :, heads], o_ref, l_ref, "shard, FP8 q.k, sampled")
+
+
+def test_fp8_qk_agrees_with_bf16_qk():
+    # The scores of the two paths differ only by the order of fp32 additions and the
+    # error of the smallest query elements (below 2^-17 of their row's largest
+    # magnitude): the LSE, computed from the scores alone, agrees to ~1e-5.  O goes
+    # through the bf16 weights P, and a score that moves a little can flip the rounding
+    # of its weight by one bf16 place (a relative 2^-8 at most); the weights sum to the
+    # denominator, so O moves by at most 2^-8 max|V|.
+    wl = wk.make_workload(None, seed=77, batch=2, q_len=2, num_heads=96, seq_lens=[3000, 1200],
+                          kv_format="fp8_e4m3fn", shuffled=True)
+    o0, l0 = run_gpu(wl, out_dtype="fp32")
+    o1, l1 = run_gpu(wl, out_dtype="fp32", fp8_qk=True)
+    do, dl = float(np.abs(o1 - o0).max()), float(np.abs(l1 - l0).max())
+    vmax = 448.0 * float(wl.kv_scale)
+    print(f"[parity] FP8 vs bf16 q.k: max|dO|={do:.3e} (bound {vmax / 256:.3e}) max|dLSE|={dl:.3e}",
+          flush=True)
+    assert dl <= 1e-4, dl
+    assert do <= vmax / 256, (do, vmax)
+
+
+@pytest.mark.parametrize("fp8_qk", [False, True], ids=["bf16qk", "fp8qk"])
+def test_query_dynamic_range(fp8_qk):
+    # rows whose largest magnitude is far from one (the FP8 q.k path's power-of-two row
+    # scale) and a row of zeros (scale 1, uniform weights).  The FP8 matrix cores' dot
+    # products hold about 17 significant bits of the score (measured: a row times 64,
+    # LSE 359, came out 2.4e-3 off, where exact sums of the same hi + lo give 5e-5), so
+    # the FP8 case stops at a row times 8 (LSE about 45)
+    import dataclasses
+
+    wl = wk.make_workload(None, seed=78, batch=1, q_len=1, num_heads=48, seq_lens=[700],
+                          kv_format="fp8_e4m3fn", shuffled=True)
+    q = wl.q_bits.copy()
+    f = (q.astype(np.uint32) << 16).view(np.float32)
+    for h, k in ((0, -20), (1, 3 if fp8_qk else 6), (2, -126), (17, 2 if fp8_qk else 3), (40, -3)):
+        f[:, :, h] *= np.float32(2.0 ** k) if k > -126 else np.float32(0.0)
+    q = (f.view(np.uint32) >> 16).astype(np.uint16)  # exact: powers of two, no subnormals
+    wl = dataclasses.replace(wl, q_bits=q)
+    check_full(wl, fp8_qk=fp8_qk)
 
 
 @pytest.mark.parametrize("partial", ["fp32", "bf16"])
