@@ -304,8 +304,13 @@ struct PageCopy {
   // (wait_vmcnt), and they complete in issue order with the other vector-memory ops.
   __device__ __forceinline__ void operator()(uint32_t base, const unsigned char* src,
                                              int valid_rows) const {
+    part<0, kPer>(base, src, valid_rows);
+  }
+  // Operations J0 .. J1 - 1 of this wave's kPer (a copy may be issued in several parts).
+  template <int J0, int J1>
+  __device__ __forceinline__ void part(uint32_t base, const unsigned char* src, int valid_rows) const {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = J0; j < (J1 < kPer ? J1 : kPer); ++j) {
       int off = src_off[j];
       if (valid_rows < kPage) {
         const int row = (block(j) * 64 + lane) / TG::kChunksPerRow;
@@ -574,6 +579,26 @@ __device__ __forceinline__ void partial_ks(
            min(kPage, L - lp * kPage));
     };
     auto issue = [&](int i) { issue_id(i, page_id(i)); };
+    // The same copy recorded, then issued in parts (pc_*): a CU queues only about twenty
+    // page-copy operations before the issuing waves stall, and with four tiles a copy has
+    // three pages to land, so the FP8 kernels spread each copy over the three phases of a
+    // page.
+    uint32_t pc_base = 0;
+    const unsigned char* pc_src = pool;
+    int pc_valid = kPage;
+    bool pc_go = false;
+    auto record_copy = [&](int i, int32_t id) {
+      pc_go = i < n;
+      if (!pc_go) return;
+      const int lp = pb + i;
+      if ((uint64_t)(int64_t)id >= (uint64_t)args.npages) {
+        bad = true;
+        id = 0;
+      }
+      pc_base = tiles_lds + (i % kTiles) * TG::kPageBytes;
+      pc_src = pool + (int64_t)id * TG::kPageBytes;
+      pc_valid = min(kPage, L - lp * kPage);
+    };
 
     // ---- queries through LDS (one HBM read per workgroup), then the first pages
     unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
@@ -654,6 +679,11 @@ __device__ __forceinline__ void partial_ks(
     // bf16 kernel (mostly a few pages per piece) measured faster with the copy of page
     // i + kTiles issued after a barrier at the end of page i.
     constexpr bool kTopIssue = FP8 || RBW == 2;
+    // FP8 (four tiles): a top-issued copy goes out in parts, operations [0, kS1) at the
+    // top, [kS1, kS2) after the row-max barrier, the rest after the P^T barrier (two
+    // bf16 tiles leave a copy one page to land: all of it at the top)
+    constexpr bool kSpread = kTopIssue && kTiles >= 4;
+    constexpr int kS1 = 2, kS2 = 4;
     int32_t next_id = kTopIssue ? page_id(kTiles) : 0;
     for (int i = 0; i < n; ++i) {
       // the pages issued after page i may stay in flight (top issue: kTiles - 1 of them
@@ -663,7 +693,11 @@ __device__ __forceinline__ void partial_ks(
       else
         wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
       barrier_lds();  // every wave's copies of page i have landed
-      if constexpr (kTopIssue) {
+      if constexpr (kSpread) {
+        pc_go = false;
+        if (i > 0) record_copy(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
+        if (pc_go) copy.template part<0, kS1>(pc_base, pc_src, pc_valid);
+      } else if constexpr (kTopIssue) {
         if (i > 0) issue_id(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
       }
       const unsigned char* tile = tiles + (i % kTiles) * TG::kPageBytes;
@@ -817,6 +851,9 @@ __device__ __forceinline__ void partial_ks(
         }
       }
       barrier_lds();
+      if constexpr (kSpread) {
+        if (pc_go) copy.template part<kS1, kS2>(pc_base, pc_src, pc_valid);
+      }
 
       // ---- online softmax update; half 0 builds P^T of its sub-tile for every wave.  The
       // running max is exact (the largest weight of a row is exactly 1 in bf16); O is
@@ -867,6 +904,9 @@ __device__ __forceinline__ void partial_ks(
         }
       }
       barrier_lds();
+      if constexpr (kSpread) {
+        if (pc_go) copy.template part<kS2, kPer>(pc_base, pc_src, pc_valid);
+      }
 
       // ---- O^T += V^T P^T for this wave's 64 columns of every row block
       if constexpr (!kEarlyV) read_v();
