@@ -580,9 +580,8 @@ __device__ __forceinline__ void partial_ks(
     };
     auto issue = [&](int i) { issue_id(i, page_id(i)); };
     // The same copy recorded, then issued in parts (pc_*): a CU queues only about twenty
-    // page-copy operations before the issuing waves stall, and with four tiles a copy has
-    // three pages to land, so the FP8 kernels spread each copy over the three phases of a
-    // page.
+    // page-copy operations before the issuing waves stall, so the multi-row and FP8
+    // kernels spread each copy over the phases of a page.
     uint32_t pc_base = 0;
     const unsigned char* pc_src = pool;
     int pc_valid = kPage;
@@ -679,11 +678,12 @@ __device__ __forceinline__ void partial_ks(
     // bf16 kernel (mostly a few pages per piece) measured faster with the copy of page
     // i + kTiles issued after a barrier at the end of page i.
     constexpr bool kTopIssue = FP8 || RBW == 2;
-    // FP8 (four tiles): a top-issued copy goes out in parts, operations [0, kS1) at the
-    // top, [kS1, kS2) after the row-max barrier, the rest after the P^T barrier (two
-    // bf16 tiles leave a copy one page to land: all of it at the top)
-    constexpr bool kSpread = kTopIssue && kTiles >= 4;
-    constexpr int kS1 = 2, kS2 = 4;
+    // Parts of a top-issued copy: operations [0, kS1) at the top, [kS1, kS2) after the
+    // row-max barrier, the rest after the P^T barrier.  With four FP8 tiles a copy has
+    // three pages to land (2 + 2 + 1 of five); with two bf16 tiles it must land within
+    // the page, so two thirds go at the top and the rest after the row-max barrier
+    // (6 + 3 of nine; 5 + 4, 4 + 5, 3 + 3 + 3 and 7 + 2 measured slower).
+    constexpr int kS1 = kTiles >= 4 ? 2 : 6, kS2 = kTiles >= 4 ? 4 : kPer;
     int32_t next_id = kTopIssue ? page_id(kTiles) : 0;
     for (int i = 0; i < n; ++i) {
       // the pages issued after page i may stay in flight (top issue: kTiles - 1 of them
@@ -693,12 +693,10 @@ __device__ __forceinline__ void partial_ks(
       else
         wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
       barrier_lds();  // every wave's copies of page i have landed
-      if constexpr (kSpread) {
+      if constexpr (kTopIssue) {
         pc_go = false;
         if (i > 0) record_copy(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
         if (pc_go) copy.template part<0, kS1>(pc_base, pc_src, pc_valid);
-      } else if constexpr (kTopIssue) {
-        if (i > 0) issue_id(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
       }
       const unsigned char* tile = tiles + (i % kTiles) * TG::kPageBytes;
       const int lp = pb + i;
@@ -851,7 +849,7 @@ __device__ __forceinline__ void partial_ks(
         }
       }
       barrier_lds();
-      if constexpr (kSpread) {
+      if constexpr (kTopIssue) {
         if (pc_go) copy.template part<kS1, kS2>(pc_base, pc_src, pc_valid);
       }
 
@@ -904,7 +902,7 @@ __device__ __forceinline__ void partial_ks(
         }
       }
       barrier_lds();
-      if constexpr (kSpread) {
+      if constexpr (kTopIssue) {
         if (pc_go) copy.template part<kS2, kPer>(pc_base, pc_src, pc_valid);
       }
 
