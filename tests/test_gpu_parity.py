@@ -471,6 +471,22 @@ def test_out_of_range_page_gives_nan_not_fault():
     compare(wl, o[[0, 2]], l[[0, 2]], o_ref, l_ref, "other requests")
 
 
+@pytest.mark.parametrize("kv,T,H", [("bf16", 1, 16), ("bf16", 4, 16), ("fp8_e4m3fn", 1, 16),
+                                    ("fp8_e4m3fn", 1, 96)],
+                         ids=["bf16-1block", "bf16-2blocks", "fp8-1block", "fp8-2blocks"])
+def test_out_of_range_page_inside_the_page_loop(kv, T, H):
+    """The same with the bad id on page 10 of a 16-page piece: its copy is issued from
+    inside the page loop (in parts, for the kernels that split their copies)."""
+    wl = wk.make_workload(None, seed=531, batch=3, q_len=T, num_heads=H, seq_lens=[1000, 1000, 1000],
+                          kv_format=kv)
+    bad = wl.block_table.copy()
+    bad[1, 10] = -7
+    o, l = run_gpu(wl, num_splits=1, block_table=bad)
+    assert np.isnan(l[1]).all() and np.isnan(o[1]).all()
+    o_ref, l_ref = run_oracle(wl, requests=[0, 2])
+    compare(wl, o[[0, 2]], l[[0, 2]], o_ref, l_ref, "other requests")
+
+
 # ------------------------------------------------------------ workspace layout
 
 @pytest.mark.parametrize("partial", ["bf16", "fp32"])
