@@ -484,7 +484,9 @@ struct KSplitSmem {
   using C = KSplitCfg<FP8, RBW>;
   __attribute__((aligned(1024))) unsigned char tiles[C::kTiles * C::TG::kPageBytes];
   f32x4 sx[RBW == 2 ? 1 : RBW][4][64];  // k-half 1 partial scores (not used with two row blocks)
-  __attribute__((aligned(16))) unsigned char pbuf[RBW][2 * 64 * 16];  // P^T of the page, bf16
+  // P^T of the page (bf16); the FP8 row split keeps two pages'
+  static constexpr int kPbufBytes = 2 * 64 * 16 * (FP8 && RBW == 2 ? 2 : 1);
+  __attribute__((aligned(16))) unsigned char pbuf[RBW][kPbufBytes];
   float red[RBW][4 * 16];                                             // row maxima of the sub-tiles
   float red2[RBW][4 * 16];                                            // row denominators (epilogue)
 };
@@ -671,262 +673,419 @@ __device__ __forceinline__ void partial_ks(
       for (int ct = 0; ct < CT; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Multi-row and FP8 kernels: the copy of page i + kTiles - 1 goes out as soon as page i
-    // has landed everywhere.  The barrier that says so also says every wave is done with
-    // page i - 1, whose tile it reuses, so no barrier of its own is needed, and its
-    // block-table entry is read one page earlier, off the critical path.  The one-row-block
-    // bf16 kernel (mostly a few pages per piece) measured faster with the copy of page
-    // i + kTiles issued after a barrier at the end of page i.
-    constexpr bool kTopIssue = FP8 || RBW == 2;
-    // Parts of a top-issued copy: operations [0, kS1) at the top, [kS1, kS2) after the
-    // row-max barrier, the rest after the P^T barrier.  With four FP8 tiles a copy has
-    // three pages to land (2 + 2 + 1 of five); with two bf16 tiles it must land within
-    // the page, so two thirds go at the top and the rest after the row-max barrier
-    // (6 + 3 of nine; 5 + 4, 4 + 5, 3 + 3 + 3 and 7 + 2 measured slower).
-    constexpr int kS1 = kTiles >= 4 ? 2 : 6, kS2 = kTiles >= 4 ? 4 : kPer;
-    int32_t next_id = kTopIssue ? page_id(kTiles) : 0;
-    for (int i = 0; i < n; ++i) {
-      // the pages issued after page i may stay in flight (top issue: kTiles - 1 of them
-      // before the loop's first copy, kTiles - 2 afterwards)
-      if constexpr (kTopIssue)
-        wait_pages<kPer, kTiles - 1>(min(n, i == 0 ? kTiles : i + kTiles - 1) - (i + 1));
-      else
-        wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
-      barrier_lds();  // every wave's copies of page i have landed
-      if constexpr (kTopIssue) {
-        pc_go = false;
-        if (i > 0) record_copy(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
-        if (pc_go) copy.template part<0, kS1>(pc_base, pc_src, pc_valid);
-      }
-      const unsigned char* tile = tiles + (i % kTiles) * TG::kPageBytes;
-      const int lp = pb + i;
-
-      // ---- partial S^T of sub-tile u over this wave's k-half, then the V^T operands of
-      // this wave's output columns (both 32-position chunks; they do not depend on the
-      // softmax, so these transposing reads run under the MFMAs and the exchanges)
-      const unsigned char* kt = tile + u * 16 * TG::kRowBytes;
-      bf16x8 kf[KQ];
-      i32x2 kr[KQ];  // F8QK: the codes as they are
+    // FP8 with the row split: two pages an iteration.  One row-max exchange and one P^T
+    // exchange serve both pages, and the scores of the two pages are four independent
+    // MFMA chains.  The copies of pages i + 2 and i + 3 go out once pages i and i + 1 have
+    // landed everywhere (into the tiles of pages i - 2 and i - 1), in parts over the
+    // phases of the iteration.
+    constexpr bool kPair = FP8 && RS;
+    static_assert(!kPair || (kTiles == 4 && kPer == 5), "pair plan: four tiles, five operations a page");
+    if constexpr (kPair) {
+      // scores of sub-tile u for row block kh on page i (raw: the scale, rsc, comes later)
+      auto qk = [&](int i) -> f32x4 {
+        const unsigned char* kt = tiles + (i % kTiles) * TG::kPageBytes + u * 16 * TG::kRowBytes;
+        f32x4 a[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if constexpr (F8QK) {
+          // block b's operand: the codes of k-steps 4b, 4b+2, 4b+1, 4b+3 (see the queries)
+          i32x2 kr[KQ];
 #pragma unroll
-      for (int s = 0; s < KQ; ++s) {
-        const int kk = RS ? s : kh * KS + s;
-        const unsigned char* ka =
-            kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1) + OperandAddr<FP8>::kstep(kk);
-        if constexpr (F8QK) kr[s] = *(const i32x2*)ka;
-        else if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
-        else kf[s] = *(const bf16x8*)ka;
-      }
-      f32x4 sp[RBW];
+          for (int s = 0; s < KQ; ++s)
+            kr[s] = *(const i32x2*)(kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, s & 1) + OperandAddr<FP8>::kstep(s));
 #pragma unroll
-      for (int j = 0; j < RBW; ++j) sp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (F8QK) {
-        // the key codes sit at the same bytes of each operand as the query elements of
-        // their columns; hi and lo accumulate apart (two independent chains)
+          for (int b = 0; b < 4; ++b) {
+            const i32x8 k8 = i32x8{kr[4 * b][0], kr[4 * b][1], kr[4 * b + 2][0], kr[4 * b + 2][1],
+                                   kr[4 * b + 1][0], kr[4 * b + 1][1], kr[4 * b + 3][0], kr[4 * b + 3][1]};
+            a[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8h[b], a[0], 0, 0, 0, 0, 0, 0);
+            a[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8l[b], a[1], 0, 0, 0, 0, 0, 0);
+          }
+          const i32x8 k8 = i32x8{kr[16][0], kr[16][1], kr[17][0], kr[17][1], kr[16][0], kr[16][1], kr[17][0], kr[17][1]};
+          a[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8t, a[0], 0, 0, 0, 0, 0, 0);
+        } else {
+          bf16x8 kf[KQ];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const i32x8 k8 = i32x8{kr[4 * b][0], kr[4 * b][1], kr[4 * b + 2][0], kr[4 * b + 2][1],
-                                 kr[4 * b + 1][0], kr[4 * b + 1][1], kr[4 * b + 3][0], kr[4 * b + 3][1]};
-          sp[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8h[b], sp[0], 0, 0, 0, 0, 0, 0);
-          sp[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8l[b], sp[1], 0, 0, 0, 0, 0, 0);
+          for (int s = 0; s < KQ; ++s)
+            kf[s] = fp8x8_to_bf16x8(*(const i32x2*)(kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, s & 1) +
+                                                    OperandAddr<FP8>::kstep(s)));
+#pragma unroll
+          for (int s = 0; s < KQ; ++s)
+            a[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[0][s]),
+                                                               a[s & 1], 0, 0, 0);
         }
-        const i32x8 k8 = i32x8{kr[16][0], kr[16][1], kr[17][0], kr[17][1], kr[16][0], kr[16][1], kr[17][0], kr[17][1]};
-        sp[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k8, q8t, sp[0], 0, 0, 0, 0, 0, 0);
-        sp[0] += sp[1];
-      } else if constexpr (RS) {
-        // two accumulators (even and odd k-steps) halve the dependent MFMA chain
+        return a[0] + a[1];
+      };
+      // positions at or past the row block's visible count (only a request's last pages)
+      auto mask = [&](int i, f32x4& sv) {
+        const int lp = pb + i;
+        if ((lp + 1) * kPage > L - lag_max) {
+          const int vis = L - (kh ? lag[RBW - 1] : lag[0]) - (lp * kPage + u * 16 + lgrp * 4);
 #pragma unroll
-        for (int s = 0; s < KQ; ++s)
-          sp[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[0][s]),
-                                                              sp[s & 1], 0, 0, 0);
-        sp[0] += sp[1];
-      } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-#pragma unroll
-          for (int j = 0; j < RBW; ++j)
-            sp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[j][s]),
-                                                            sp[j], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) sv[e] = e < vis ? sv[e] : kNegInf;
         }
-      }
-      bf16x8 va[2][CT];
-      auto read_v = [&]() {
+      };
+      // O^T += V^T P^T for this wave's 64 columns of both row blocks, page i (its P^T in
+      // half pg of the buffer)
+      auto pv = [&](int i, int pg) {
+        const unsigned char* tile = tiles + (i % kTiles) * TG::kPageBytes;
+        bf16x8 va[2][CT];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
-            const unsigned char* va0 =
-                tile + c * 32 * TG::kRowBytes + addr.vbase[ct] + OperandAddr<FP8>::vstep(ct);
-            if constexpr (FP8) {
-              va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
-            } else {
-              const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
-              const bf16x4 hi =
-                  __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
-              va[c][ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
+            const unsigned char* va0 = tile + c * 32 * TG::kRowBytes + addr.vbase[ct] + OperandAddr<FP8>::vstep(ct);
+            va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+          i32x4 p0, p1;
+          lds_read_pair_b128(pbuf_lds + j * SM::kPbufBytes + pg * 2048 + lane * 16, p0, p1);
+          const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, p0), __builtin_bit_cast(bf16x8, p1)};
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[j][ct], 0, 0, 0);
           }
         }
       };
-      // bf16 with two row blocks: no registers to spare for early V^T operands
-      constexpr bool kEarlyV = FP8 || RBW == 1;
-      if constexpr (kEarlyV) read_v();
-      if constexpr (!FP8 && RS) {
-        // four K reads ahead of the MFMAs, then one MFMA per remaining read
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      // pages i + 2 and i + 3: a wave's 2 kPer operations in three parts, page i + 2's
+      // [0, kA1) and page i + 3's [0, kB1) at the top, then [kA1, kPer) and [kB1, kB2),
+      // then page i + 3's [kB2, kPer): 5 + 4 + 1 (4 + 4 + 2, 6 + 4 and 3 + 4 + 3 measured
+      // up to 1% slower)
+      constexpr int kA1 = 5, kB1 = 0, kB2 = 4;
+      uint32_t cb[2] = {0, 0};
+      const unsigned char* cs[2] = {pool, pool};
+      int cv[2] = {kPage, kPage};
+      bool cg[2] = {false, false};
+      auto record_pair = [&](int i, int32_t id0, int32_t id1) {
 #pragma unroll
-        for (int s = 0; s < KQ - 4; ++s) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int k = 0; k < 2; ++k) {
+          const int ip = i + k;
+          int32_t id = k ? id1 : id0;
+          cg[k] = ip < n;
+          if (!cg[k]) continue;
+          if ((uint64_t)(int64_t)id >= (uint64_t)args.npages) {
+            bad = true;
+            id = 0;
+          }
+          cb[k] = tiles_lds + (ip % kTiles) * TG::kPageBytes;
+          cs[k] = pool + (int64_t)id * TG::kPageBytes;
+          cv[k] = min(kPage, L - (pb + ip) * kPage);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      } else if constexpr (!FP8 && RBW == 1) {
-        // instruction order: six K reads ahead of the MFMAs, then one MFMA per remaining
-        // read; the sixteen V^T reads go between the last six MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-      } else if constexpr (!FP8) {
-        // two row blocks: four K reads ahead, then one k-step's two MFMAs per remaining read
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int s = 0; s < 5; ++s) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      }
+      };
 
-      // ---- the k-halves meet: half 1 hands its partial scores to half 0, which scales,
-      // masks and takes its sub-tile's row max (RS: every wave has whole scores)
-      if constexpr (!RS) {
-        if (kh == 1) {
-#pragma unroll
-          for (int j = 0; j < RBW; ++j) sm.sx[j][u][lane] = sp[j];
-        }
-        barrier_lds();
-      }
-      // raw scores (the scale is applied to the max and inside the exponent); positions
-      // at or past a row block's visible count are masked, which only a request's last
-      // pages need
-      f32x4 sv[RBW];
-      if constexpr (RS) {
-        sv[0] = sp[0];
-        if ((lp + 1) * kPage > L - lag_max) {
-          const int vis = L - (kh ? lag[RBW - 1] : lag[0]) - (lp * kPage + u * 16 + lgrp * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sv[0][e] = e < vis ? sv[0][e] : kNegInf;
-        }
-        float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+      int32_t nid0 = page_id(kTiles), nid1 = page_id(kTiles + 1);  // ids of pages i + 2, i + 3
+      for (int i = 0; i < n; i += 2) {
+        const bool hasB = i + 1 < n;
+        // the first pair may leave pages 2 and 3 in flight; later every page issued so
+        // far is page i + 1 or older
+        if (i == 0) wait_pages<kPer, 2>(min(n, kTiles) - 2);
+        else wait_vmcnt<0>();
+        barrier_lds();  // pages i, i + 1 landed; every wave is done with pages i - 2, i - 1
+        cg[0] = cg[1] = false;
+        if (i > 0) record_pair(i + 2, __builtin_amdgcn_readfirstlane(nid0), __builtin_amdgcn_readfirstlane(nid1));
+        if (cg[0]) copy.template part<0, kA1>(cb[0], cs[0], cv[0]);
+        if (cg[1]) copy.template part<0, kB1>(cb[1], cs[1], cv[1]);
+
+        f32x4 sa = qk(i);
+        f32x4 sb = qk(hasB ? i + 1 : i);
+        mask(i, sa);
+        if (hasB) mask(i + 1, sb);
+        else sb = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+        // (scalar loads here land under the MFMAs; they share a counter with the LDS reads)
+        nid0 = page_id(i + 4);
+        nid1 = page_id(i + 5);
+        float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                         fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
         mx = max_over_rows(mx);
         if (lgrp == 0) sm.red[kh][u * 16 + lrow] = mx * rsc;
-      } else if (kh == 0) {
-        const bool whole = (lp + 1) * kPage <= L - lag_max;
+        barrier_lds();  // both pages' row maxima
+        if (cg[0]) copy.template part<kA1, kPer>(cb[0], cs[0], cv[0]);
+        if (cg[1]) copy.template part<kB1, kB2>(cb[1], cs[1], cv[1]);
+
+        // online softmax update over both pages (exact running max; O rescaled only when
+        // some row's max grows), P^T of this wave's sub-tile of each
+        float alpha[RBW], msubs[RBW];
+        bool grown = false;
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
-          const f32x4 other = sm.sx[j][u][lane];
-          sv[j] = sp[j] + other;
-          if (!whole) {
-            const int vis = L - lag[j] - (lp * kPage + u * 16 + lgrp * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sv[j][e] = e < vis ? sv[j][e] : kNegInf;
-          }
-          float mx = fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3]));
-          mx = max_over_rows(mx);
-          if (lgrp == 0) sm.red[j][u * 16 + lrow] = mx * args.sscale;
+          const float m2 = lds_max_of<4>(red_lds + 4 * (j * 64 + lrow), kNegInf);
+          const bool grow = m2 > m[j];
+          const float m_new = grow ? m2 : m[j];
+          const float msub = m_new == kNegInf ? 0.f : m_new;
+          msubs[j] = msub;
+          alpha[j] = grow ? exp2_fast(m[j] - msub) : 1.f;
+          grown |= grow;
+          m[j] = m_new;
         }
-      }
-      barrier_lds();
-      if constexpr (kTopIssue) {
-        if (pc_go) copy.template part<kS1, kS2>(pc_base, pc_src, pc_valid);
-      }
-
-      // ---- online softmax update; half 0 builds P^T of its sub-tile for every wave.  The
-      // running max is exact (the largest weight of a row is exactly 1 in bf16); O is
-      // rescaled only on pages that raise some row's max, which become rare as the piece
-      // goes on.
-      float alpha[RBW], msubs[RBW];
-      bool grown = false;
-#pragma unroll
-      for (int j = 0; j < RBW; ++j) {
-        const float mx = lds_max_of<4>(red_lds + 4 * (j * 64 + lrow), kNegInf);
-        const bool grow = mx > m[j];  // m = -inf: any finite max
-        const float m_new = grow ? mx : m[j];
-        const float msub = m_new == kNegInf ? 0.f : m_new;
-        msubs[j] = msub;
-        alpha[j] = grow ? exp2_fast(m[j] - msub) : 1.f;  // m = -inf -> 0
-        grown |= grow;
-        m[j] = m_new;
-        if (!RS && kh == 0) {
-          float ps = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[j][e] = exp2_fast(fmaf(sv[j][e], args.sscale, -msub));
-            ps += sv[j][e];
-          }
-          lsum[j] = fmaf(lsum[j], alpha[j], ps);
-          *(bf16x4*)(sm.pbuf[j] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
-              bf16x4{(__bf16)sv[j][0], (__bf16)sv[j][1], (__bf16)sv[j][2], (__bf16)sv[j][3]};
-        }
-      }
-      if constexpr (RS) {  // this wave's sub-tile of its row block
         const float msub = kh ? msubs[RBW - 1] : msubs[0];
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sv[0][e] = exp2_fast(fmaf(sv[0][e], rsc, -msub));
-          ps += sv[0][e];
+          sa[e] = exp2_fast(fmaf(sa[e], rsc, -msub));
+          sb[e] = exp2_fast(fmaf(sb[e], rsc, -msub));  // -inf (no page B) -> 0
+          ps += sa[e] + sb[e];
         }
         lsum[0] = fmaf(lsum[0], kh ? alpha[RBW - 1] : alpha[0], ps);
-        *(bf16x4*)(sm.pbuf[kh] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
-            bf16x4{(__bf16)sv[0][0], (__bf16)sv[0][1], (__bf16)sv[0][2], (__bf16)sv[0][3]};
+        unsigned char* pw = sm.pbuf[kh] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8;
+        *(bf16x4*)pw = bf16x4{(__bf16)sa[0], (__bf16)sa[1], (__bf16)sa[2], (__bf16)sa[3]};
+        *(bf16x4*)(pw + 2048) = bf16x4{(__bf16)sb[0], (__bf16)sb[1], (__bf16)sb[2], (__bf16)sb[3]};
+        if (__builtin_amdgcn_ballot_w64(grown)) {
+#pragma unroll
+          for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[j][ct] *= alpha[j];
+          }
+        }
+        barrier_lds();  // both pages' P^T
+        if (cg[1]) copy.template part<kB2, kPer>(cb[1], cs[1], cv[1]);
+
+        pv(i, 0);
+        if (hasB) pv(i + 1, 1);
       }
-      // every lane of every wave sees the same maxima, so the branch is uniform
-      if (__builtin_amdgcn_ballot_w64(grown)) {
+    } else {
+      // Multi-row and FP8 kernels: the copy of page i + kTiles - 1 goes out as soon as page i
+      // has landed everywhere.  The barrier that says so also says every wave is done with
+      // page i - 1, whose tile it reuses, so no barrier of its own is needed, and its
+      // block-table entry is read one page earlier, off the critical path.  The one-row-block
+      // bf16 kernel (mostly a few pages per piece) measured faster with the copy of page
+      // i + kTiles issued after a barrier at the end of page i.
+      constexpr bool kTopIssue = FP8 || RBW == 2;
+      // Parts of a top-issued copy: operations [0, kS1) at the top, [kS1, kS2) after the
+      // row-max barrier, the rest after the P^T barrier.  With four FP8 tiles a copy has
+      // three pages to land (2 + 2 + 1 of five); with two bf16 tiles it must land within
+      // the page, so two thirds go at the top and the rest after the row-max barrier
+      // (6 + 3 of nine; 5 + 4, 4 + 5, 3 + 3 + 3 and 7 + 2 measured slower).
+      constexpr int kS1 = kTiles >= 4 ? 2 : 6, kS2 = kTiles >= 4 ? 4 : kPer;
+      int32_t next_id = kTopIssue ? page_id(kTiles) : 0;
+      for (int i = 0; i < n; ++i) {
+        // the pages issued after page i may stay in flight (top issue: kTiles - 1 of them
+        // before the loop's first copy, kTiles - 2 afterwards)
+        if constexpr (kTopIssue)
+          wait_pages<kPer, kTiles - 1>(min(n, i == 0 ? kTiles : i + kTiles - 1) - (i + 1));
+        else
+          wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
+        barrier_lds();  // every wave's copies of page i have landed
+        if constexpr (kTopIssue) {
+          pc_go = false;
+          if (i > 0) record_copy(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
+          if (pc_go) copy.template part<0, kS1>(pc_base, pc_src, pc_valid);
+        }
+        const unsigned char* tile = tiles + (i % kTiles) * TG::kPageBytes;
+        const int lp = pb + i;
+
+        // ---- partial S^T of sub-tile u over this wave's k-half, then the V^T operands of
+        // this wave's output columns (both 32-position chunks; they do not depend on the
+        // softmax, so these transposing reads run under the MFMAs and the exchanges)
+        const unsigned char* kt = tile + u * 16 * TG::kRowBytes;
+        bf16x8 kf[KQ];
+#pragma unroll
+        for (int s = 0; s < KQ; ++s) {
+          const int kk = RS ? s : kh * KS + s;
+          const unsigned char* ka =
+              kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1) + OperandAddr<FP8>::kstep(kk);
+          if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
+          else kf[s] = *(const bf16x8*)ka;
+        }
+        f32x4 sp[RBW];
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) sp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (RS) {
+          // two accumulators (even and odd k-steps) halve the dependent MFMA chain
+#pragma unroll
+          for (int s = 0; s < KQ; ++s)
+            sp[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[0][s]),
+                                                                sp[s & 1], 0, 0, 0);
+          sp[0] += sp[1];
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int j = 0; j < RBW; ++j)
+              sp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], __builtin_bit_cast(bf16x8, qf[j][s]),
+                                                              sp[j], 0, 0, 0);
+          }
+        }
+        bf16x8 va[2][CT];
+        auto read_v = [&]() {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              const unsigned char* va0 =
+                  tile + c * 32 * TG::kRowBytes + addr.vbase[ct] + OperandAddr<FP8>::vstep(ct);
+              if constexpr (FP8) {
+                va[c][ct] = fp8x8_to_bf16x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)va0));
+              } else {
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)va0);
+                const bf16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + 16 * TG::kRowBytes));
+                va[c][ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              }
+            }
+          }
+        };
+        // bf16 with two row blocks: no registers to spare for early V^T operands
+        constexpr bool kEarlyV = FP8 || RBW == 1;
+        if constexpr (kEarlyV) read_v();
+        if constexpr (!FP8 && RS) {
+          // four K reads ahead of the MFMAs, then one MFMA per remaining read
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int s = 0; s < KQ - 4; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        } else if constexpr (!FP8 && RBW == 1) {
+          // instruction order: six K reads ahead of the MFMAs, then one MFMA per remaining
+          // read; the sixteen V^T reads go between the last six MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+          for (int s = 0; s < 3; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+          }
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        } else if constexpr (!FP8) {
+          // two row blocks: four K reads ahead, then one k-step's two MFMAs per remaining read
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int s = 0; s < 5; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+
+        // ---- the k-halves meet: half 1 hands its partial scores to half 0, which scales,
+        // masks and takes its sub-tile's row max (RS: every wave has whole scores)
+        if constexpr (!RS) {
+          if (kh == 1) {
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) sm.sx[j][u][lane] = sp[j];
+          }
+          barrier_lds();
+        }
+        // raw scores (the scale is applied to the max and inside the exponent); positions
+        // at or past a row block's visible count are masked, which only a request's last
+        // pages need
+        f32x4 sv[RBW];
+        if constexpr (RS) {
+          sv[0] = sp[0];
+          if ((lp + 1) * kPage > L - lag_max) {
+            const int vis = L - (kh ? lag[RBW - 1] : lag[0]) - (lp * kPage + u * 16 + lgrp * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[0][e] = e < vis ? sv[0][e] : kNegInf;
+          }
+          float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+          mx = max_over_rows(mx);
+          if (lgrp == 0) sm.red[kh][u * 16 + lrow] = mx * rsc;
+        } else if (kh == 0) {
+          const bool whole = (lp + 1) * kPage <= L - lag_max;
+#pragma unroll
+          for (int j = 0; j < RBW; ++j) {
+            const f32x4 other = sm.sx[j][u][lane];
+            sv[j] = sp[j] + other;
+            if (!whole) {
+              const int vis = L - lag[j] - (lp * kPage + u * 16 + lgrp * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sv[j][e] = e < vis ? sv[j][e] : kNegInf;
+            }
+            float mx = fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3]));
+            mx = max_over_rows(mx);
+            if (lgrp == 0) sm.red[j][u * 16 + lrow] = mx * args.sscale;
+          }
+        }
+        barrier_lds();
+        if constexpr (kTopIssue) {
+          if (pc_go) copy.template part<kS1, kS2>(pc_base, pc_src, pc_valid);
+        }
+
+        // ---- online softmax update; half 0 builds P^T of its sub-tile for every wave.  The
+        // running max is exact (the largest weight of a row is exactly 1 in bf16); O is
+        // rescaled only on pages that raise some row's max, which become rare as the piece
+        // goes on.
+        float alpha[RBW], msubs[RBW];
+        bool grown = false;
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
+          const float mx = lds_max_of<4>(red_lds + 4 * (j * 64 + lrow), kNegInf);
+          const bool grow = mx > m[j];  // m = -inf: any finite max
+          const float m_new = grow ? mx : m[j];
+          const float msub = m_new == kNegInf ? 0.f : m_new;
+          msubs[j] = msub;
+          alpha[j] = grow ? exp2_fast(m[j] - msub) : 1.f;  // m = -inf -> 0
+          grown |= grow;
+          m[j] = m_new;
+          if (!RS && kh == 0) {
+            float ps = 0.f;
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) acc[j][ct] *= alpha[j];
+            for (int e = 0; e < 4; ++e) {
+              sv[j][e] = exp2_fast(fmaf(sv[j][e], args.sscale, -msub));
+              ps += sv[j][e];
+            }
+            lsum[j] = fmaf(lsum[j], alpha[j], ps);
+            *(bf16x4*)(sm.pbuf[j] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
+                bf16x4{(__bf16)sv[j][0], (__bf16)sv[j][1], (__bf16)sv[j][2], (__bf16)sv[j][3]};
+          }
         }
-      }
-      barrier_lds();
-      if constexpr (kTopIssue) {
-        if (pc_go) copy.template part<kS2, kPer>(pc_base, pc_src, pc_valid);
-      }
+        if constexpr (RS) {  // this wave's sub-tile of its row block
+          const float msub = kh ? msubs[RBW - 1] : msubs[0];
+          float ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[0][e] = exp2_fast(fmaf(sv[0][e], rsc, -msub));
+            ps += sv[0][e];
+          }
+          lsum[0] = fmaf(lsum[0], kh ? alpha[RBW - 1] : alpha[0], ps);
+          *(bf16x4*)(sm.pbuf[kh] + ((u >> 1) * 64 + lane) * 16 + (u & 1) * 8) =
+              bf16x4{(__bf16)sv[0][0], (__bf16)sv[0][1], (__bf16)sv[0][2], (__bf16)sv[0][3]};
+        }
+        // every lane of every wave sees the same maxima, so the branch is uniform
+        if (__builtin_amdgcn_ballot_w64(grown)) {
+#pragma unroll
+          for (int j = 0; j < RBW; ++j) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[j][ct] *= alpha[j];
+          }
+        }
+        barrier_lds();
+        if constexpr (kTopIssue) {
+          if (pc_go) copy.template part<kS2, kPer>(pc_base, pc_src, pc_valid);
+        }
 
-      // ---- O^T += V^T P^T for this wave's 64 columns of every row block
-      if constexpr (!kEarlyV) read_v();
+        // ---- O^T += V^T P^T for this wave's 64 columns of every row block
+        if constexpr (!kEarlyV) read_v();
 #pragma unroll
-      for (int j = 0; j < RBW; ++j) {
-        i32x4 p0, p1;
-        lds_read_pair_b128(pbuf_lds + j * (2 * 64 * 16) + lane * 16, p0, p1);
-        const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, p0), __builtin_bit_cast(bf16x8, p1)};
+        for (int j = 0; j < RBW; ++j) {
+          i32x4 p0, p1;
+          lds_read_pair_b128(pbuf_lds + j * SM::kPbufBytes + lane * 16, p0, p1);
+          const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, p0), __builtin_bit_cast(bf16x8, p1)};
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+          for (int c = 0; c < 2; ++c) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[j][ct], 0, 0, 0);
+            for (int ct = 0; ct < CT; ++ct)
+              acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[c][ct], pf[c], acc[j][ct], 0, 0, 0);
+          }
         }
-      }
-      if constexpr (kTopIssue) {
-        // (a scalar load here lands under the MFMAs; earlier, it would hold up the first
-        // wait for the page's LDS reads, which shares its counter)
-        if (i > 0) next_id = page_id(i + kTiles);
-      } else if (i + kTiles < n) {
-        barrier_lds();  // every wave is done with this tile
-        issue(i + kTiles);
+        if constexpr (kTopIssue) {
+          // (a scalar load here lands under the MFMAs; earlier, it would hold up the first
+          // wait for the page's LDS reads, which shares its counter)
+          if (i > 0) next_id = page_id(i + kTiles);
+        } else if (i + kTiles < n) {
+          barrier_lds();  // every wave is done with this tile
+          issue(i + kTiles);
+        }
       }
     }
 
