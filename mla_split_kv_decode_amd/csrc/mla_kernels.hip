@@ -209,8 +209,12 @@ struct TileGeom {
   __device__ static constexpr int key16(int row) {
     return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
   }
+  // fp8: 576-byte rows 4 apart start on the same bank and so do rows 16 apart; the key
+  // separates both within a 64-byte group (the transposing V^T reads take rows r and
+  // r + 16 together)
+  __device__ static constexpr int key8(int row) { return ((row >> 2) & 3) ^ (((row >> 4) & 1) << 1); }
   __device__ static __forceinline__ int swz(int row, int c) {
-    if constexpr (FP8) return (c & ~3) | ((c & 3) ^ ((row >> 2) & 3));
+    if constexpr (FP8) return (c & ~3) | ((c & 3) ^ key8(row));
     else return (c & ~7) | ((c & 7) ^ key16(row));
   }
   __device__ static __forceinline__ int offset(int row, int chunk) {
@@ -228,33 +232,32 @@ struct TileGeom {
 // compile-time offset (an instruction immediate).
 //
 // K (A operand of QK^T), 16x32 block of sub-tile pt and k-step kk:
-//   kbase[kk & 1] + pt * 16 * kRowBytes + kstep(kk)
+//   kbase_of(lrow, lgrp, kk & 1, pt) + pt * 16 * kRowBytes + kstep(kk)
 // V^T (A operand of PV), 32-position chunk c, half hh (positions +16), column tile ct of
 // this wave: vbase[ct & 3] + c * 32 * kRowBytes + hh * 16 * kRowBytes + vstep(ct)
 template <bool FP8>
 struct OperandAddr {
   using TG = TileGeom<FP8>;
-  int kbase[2];
+  int kbase[2];  // kbase_of(lrow, lgrp, e, 0)
   int vbase[4];
   __device__ __forceinline__ OperandAddr(int lrow, int lgrp, int wave_col_tile0) {
     if constexpr (FP8) {
-      // K: row 16pt+lrow, chunk 2kk + (lgrp>>1), byte 8(lgrp&1); key (lrow>>2)&3
-      const int key = (lrow >> 2) & 3;
+      const int kkey = TG::key8(lrow);
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        kbase[e] = lrow * TG::kRowBytes + 16 * ((2 * e + (lgrp >> 1)) ^ key) + 8 * (lgrp & 1);
+        kbase[e] = lrow * TG::kRowBytes + 16 * ((2 * e + (lgrp >> 1)) ^ kkey) + 8 * (lgrp & 1);
       // V^T (tr8): lane (lgrp, lrow = 2ii + h) reads row 32c + 16(ii>>2) + 4 lgrp + (ii&3),
-      // chunk n = wave_col_tile0 + ct, byte 8h; key = lgrp
+      // chunk n = wave_col_tile0 + ct, byte 8h; key8 of the row = lgrp ^ 2 ((ii>>2) & 1)
       const int ii = lrow >> 1, h = lrow & 1;
       const int row = 16 * (ii >> 2) + 4 * lgrp + (ii & 3);
+      const int key = TG::key8(row);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        vbase[j] = row * TG::kRowBytes + 16 * (4 * (wave_col_tile0 >> 2) + (j ^ lgrp)) + 8 * h;
+        vbase[j] = row * TG::kRowBytes + 16 * (4 * (wave_col_tile0 >> 2) + (j ^ key)) + 8 * h;
     } else {
-      // K: row 16pt+lrow, chunk 4kk + lgrp; key key16(lrow)
-      const int key = TG::key16(lrow);
+      const int kkey = TG::key16(lrow);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) kbase[e] = lrow * TG::kRowBytes + 16 * ((4 * e + lgrp) ^ key);
+      for (int e = 0; e < 2; ++e) kbase[e] = lrow * TG::kRowBytes + 16 * ((4 * e + lgrp) ^ kkey);
       // V^T (tr16): row 32c + 16hh + 4 lgrp + (lrow>>2), chunk 2n + ((lrow&3)>>1) with
       // n = wave_col_tile0 + ct, byte 8(lrow&1); key key16 of the row
       const int key_v = TG::key16(4 * lgrp + (lrow >> 2));
@@ -267,10 +270,12 @@ struct OperandAddr {
     }
   }
   __device__ static constexpr int kstep(int kk) { return (FP8 ? 64 : 128) * (kk >> 1); }
-  // kbase[e] computed from e (for k-steps whose parity is known only at run time)
-  __device__ static __forceinline__ int kbase_of(int lrow, int lgrp, int e) {
+  // K of sub-tile pt (rows 16 pt + lrow), k-step parity e:
+  //   fp8: chunk 2kk + (lgrp>>1), byte 8(lgrp&1), key8 of the row (depends on pt's parity);
+  //   bf16: chunk 4kk + lgrp, key16 of the row (the same for every pt)
+  __device__ static __forceinline__ int kbase_of(int lrow, int lgrp, int e, int pt) {
     if constexpr (FP8)
-      return lrow * TG::kRowBytes + 16 * ((2 * e + (lgrp >> 1)) ^ ((lrow >> 2) & 3)) + 8 * (lgrp & 1);
+      return lrow * TG::kRowBytes + 16 * ((2 * e + (lgrp >> 1)) ^ TG::key8(16 * pt + lrow)) + 8 * (lgrp & 1);
     else
       return lrow * TG::kRowBytes + 16 * ((4 * e + lgrp) ^ TG::key16(lrow));
   }
@@ -620,7 +625,7 @@ __device__ __forceinline__ void partial_ks(
       for (int s = 0; s < KQ; ++s) {
         const int kk = RS ? s : kh * KS + s;  // depends on the wave: offsets computed, not indexed
         const int jr = RS ? kh : j;
-        const int kb = OperandAddr<false>::kbase_of(lrow, lgrp, kk & 1);
+        const int kb = OperandAddr<false>::kbase_of(lrow, lgrp, kk & 1, 0);
         qf[j][s] = *(const i32x4*)(stage + jr * kRowsPerBlock * TileGeom<false>::kRowBytes + kb +
                                    OperandAddr<false>::kstep(kk));
       }
@@ -690,7 +695,7 @@ __device__ __forceinline__ void partial_ks(
           i32x2 kr[KQ];
 #pragma unroll
           for (int s = 0; s < KQ; ++s)
-            kr[s] = *(const i32x2*)(kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, s & 1) + OperandAddr<FP8>::kstep(s));
+            kr[s] = *(const i32x2*)(kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, s & 1, u) + OperandAddr<FP8>::kstep(s));
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const i32x8 k8 = i32x8{kr[4 * b][0], kr[4 * b][1], kr[4 * b + 2][0], kr[4 * b + 2][1],
@@ -704,7 +709,7 @@ __device__ __forceinline__ void partial_ks(
           bf16x8 kf[KQ];
 #pragma unroll
           for (int s = 0; s < KQ; ++s)
-            kf[s] = fp8x8_to_bf16x8(*(const i32x2*)(kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, s & 1) +
+            kf[s] = fp8x8_to_bf16x8(*(const i32x2*)(kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, s & 1, u) +
                                                     OperandAddr<FP8>::kstep(s)));
 #pragma unroll
           for (int s = 0; s < KQ; ++s)
@@ -883,7 +888,7 @@ __device__ __forceinline__ void partial_ks(
         for (int s = 0; s < KQ; ++s) {
           const int kk = RS ? s : kh * KS + s;
           const unsigned char* ka =
-              kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1) + OperandAddr<FP8>::kstep(kk);
+              kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1, u) + OperandAddr<FP8>::kstep(kk);
           if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
           else kf[s] = *(const bf16x8*)ka;
         }
