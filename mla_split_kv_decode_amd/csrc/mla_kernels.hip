@@ -606,14 +606,24 @@ __device__ __forceinline__ void partial_ks(
       pc_valid = min(kPage, L - lp * kPage);
     };
 
-    // ---- queries through LDS (one HBM read per workgroup), then the first pages
+    // ---- queries through LDS (one HBM read per workgroup), then the first pages.  The
+    // one-row-block bf16 kernel (mostly two pages a piece) requests the block-table
+    // entries of its first pages before the query copies, so their round trip runs under
+    // them (unconditional loads from valid entries: the piece's last page for ti >= n,
+    // block_table[0] for an empty piece); the other kernels measured faster without.
+    constexpr bool kEarlyId = !FP8 && RBW == 1;
+    int32_t first_id[kTiles];
+#pragma unroll
+    for (int ti = 0; ti < kTiles; ++ti)
+      first_id[ti] = kEarlyId ? *(n > 0 ? trow + pb + min(ti, n - 1) : block_table) : 0;
     unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
     typename C::QC(wave, lane)(tiles_lds + kEarlyTiles * TG::kPageBytes, q_ptr + (int64_t)r * args.qlen * args.heads * kDLatent, args.heads,
                                args.hgroups, g * RBW, rb_last);
     int early = 0;
 #pragma unroll
     for (int ti = 0; ti < kEarlyTiles; ++ti) {
-      issue(ti);
+      if constexpr (kEarlyId) issue_id(ti, first_id[ti]);
+      else issue(ti);
       early += ti < n ? 1 : 0;
     }
     wait_pages<kPer, kEarlyTiles>(early);  // the query copies are older: all landed
@@ -632,7 +642,10 @@ __device__ __forceinline__ void partial_ks(
     }
     barrier_lds();  // the staging tiles are free again
 #pragma unroll
-    for (int ti = kEarlyTiles; ti < kTiles; ++ti) issue(ti);
+    for (int ti = kEarlyTiles; ti < kTiles; ++ti) {
+      if constexpr (kEarlyId) issue_id(ti, first_id[ti]);
+      else issue(ti);
+    }
 
     // F8QK: each query row times a power of two 2^a that brings its largest magnitude into
     // [128, 256), split into hi + lo; the scores then come out times 2^a, which the row's
