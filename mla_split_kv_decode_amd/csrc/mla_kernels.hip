@@ -8,12 +8,17 @@
 // handled by separate workgroups; section 1 "Cache", DCP8 paragraph: a partial answer
 // carries its normalisation so pieces can be merged.
 //
-// Stage 2, mla_merge_kernel: the LSE-weighted merge of the partial answers of each row.
+// Stage 2, mla_merge_kernel / mla_merge_rows_kernel: the LSE-weighted merge of the
+// partial answers of each row.
 //
 // Data movement.  A page (64 positions x 576 latent values) is copied from HBM straight
 // into an LDS tile with global_load_lds_dwordx4 (no staging registers); two bf16 tiles
 // (four FP8 tiles) per workgroup, so the next pages stream in while the current one is
-// consumed, and a piece of two pages has its whole history in flight at once.  Within a
+// consumed, and a piece of two pages has its whole history in flight at once.  The
+// multi-row and FP8 kernels issue each copy in parts over the phases of a page (a CU
+// accepts only about twenty copy operations before the issuing waves stall), and the
+// FP8 two-row-block kernel works on two pages an iteration (one set of exchanges for
+// both).  Within a
 // tile each 16-byte chunk of a row sits at an XOR-swizzled column so that the MFMA
 // operand reads below hit distinct LDS banks; the copy fills the tile in contiguous 1 KiB
 // blocks and each lane fetches the global chunk that belongs at its slot.
@@ -24,7 +29,9 @@
 //             heads unchanged) and are never written.
 //  * QK^T   : S^T[pos][row] = sum_k K[pos][k] Q[row][k] with v_mfma_f32_16x16x32_bf16,
 //             A = 16 positions x 32 latent columns read from the LDS tile, B = the row
-//             block's queries, kept in registers for the whole piece.
+//             block's queries, kept in registers for the whole piece (on request, FP8
+//             pools: v_mfma_f32_16x16x128_f8f6f4 on the codes and split-precision FP8
+//             queries).
 //  * PV     : O^T[col][row] += sum_pos V^T[col][pos] P^T[pos][row].  The S^T accumulator
 //             layout (lane = row, 4 consecutive positions per lane) is already the B
 //             layout of the next MFMA; P takes one small LDS exchange between the waves
