@@ -167,7 +167,7 @@ int32_t mla_plan_row_groups(const mla_plan* plan);
  * holds all 96 heads).  enable = 1: the partial stage feeds the pool's E4M3FN codes to
  * the FP8 matrix cores as they are, and each query row as two E4M3FN vectors hi + lo
  * after scaling the row by a power of two (hi + lo equals every bf16 query element
- * times that power exactly, except elements below 2^-10 of the row's largest magnitude,
+ * times that power exactly, except elements below 2^-9 of the row's largest magnitude,
  * which keep an error below 2^-17 of it).  The value side is unchanged.  Off by default.
  * Needs kv_dtype = MLA_FP8_E4M3FN and q_len * ceil(num_heads/16) >= 2; otherwise
  * MLA_ERR_UNSUPPORTED (the plan is left unchanged).  enable must be 0 or 1
