@@ -271,6 +271,56 @@ def test_query_dynamic_range(fp8_qk):
     check_full(wl, fp8_qk=fp8_qk)
 
 
+# ------------------------------------------------------------ seeded random shapes
+
+def _random_cases(n, seed=11):
+    """Shapes drawn from a seeded generator: head counts with and without padding, one
+    to four query tokens (causal or not), lengths from one page's worth to a few dozen
+    pages, every split policy, both pool formats, the FP8 q.k option on FP8 multi-row
+    shapes and, now and then, bf16 partial answers."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kv = ["bf16", "fp8_e4m3fn"][rng.integers(2)]
+        T = int(rng.choice([1, 1, 2, 3, 4]))
+        H = int(rng.choice([7, 12, 16, 32, 48, 96, 128]))
+        while T * -(-H // 16) > 64:
+            H //= 2
+        B = int(rng.integers(1, 5))
+        seq = [int(rng.integers(T, 2500)) for _ in range(B)]
+        splits = int(rng.choice([0, 0, 1, 3, 16]))
+        causal = bool(rng.integers(2))
+        f8qk = kv == "fp8_e4m3fn" and T * -(-H // 16) >= 2 and bool(rng.integers(2))
+        partial = ["fp32", "bf16"][rng.integers(2)] if rng.integers(4) == 0 else "fp32"
+        cases.append((i, B, T, H, seq, splits, kv, causal, f8qk, partial))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(16), ids=lambda c: f"r{c[0]}")
+def test_random_shapes(case):
+    i, B, T, H, seq, splits, kv, causal, f8qk, partial = case
+    wl = wk.make_workload(None, seed=1000 + i, batch=B, q_len=T, num_heads=H, seq_lens=seq,
+                          kv_format=kv, shuffled=True, num_splits=splits, causal=causal)
+    o, l = run_gpu(wl, canary=True, fp8_qk=f8qk, partial=partial)
+    o_ref, l_ref = run_oracle(wl)
+    what = f"B{B} T{T} H{H} s{splits} causal={causal} fp8qk={f8qk} partial={partial}"
+    if partial == "bf16":
+        # bf16 partial answers: a second rounding of up to 2^-9 of the largest |O_p|
+        # (the option's documented cost), checked against that bound on top of the bar
+        eo = float(np.abs(o - o_ref).max())
+        vmax = 0.0  # largest |value| any request attends to
+        for r, L in enumerate(wl.seq_lens):
+            rows = oracle.gather_latents(wl.pool, wl.block_table[r], int(L), wl.page_size)[:, :512]
+            vals = (oracle.bf16_bits_to_f64(rows) if kv == "bf16"
+                    else oracle.e4m3fn_codes_to_f64(rows) * float(wl.kv_scale))
+            vmax = max(vmax, float(np.abs(vals).max()))
+        print(f"[parity] random {what}: max|dO|={eo:.3e} (bar {TOL_O[kv] + vmax / 512:.3e})", flush=True)
+        assert eo <= TOL_O[kv] + vmax / 512, (what, eo)
+        assert float(np.abs(l - l_ref).max()) <= TOL_LSE
+    else:
+        compare(wl, o, l, o_ref, l_ref, what)
+
+
 @pytest.mark.parametrize("partial", ["fp32", "bf16"])
 def test_spec_verify_sampled(partial):
     wl = wk.make_workload("spec_verify")
