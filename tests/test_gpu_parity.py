@@ -375,6 +375,66 @@ def test_dcp_shard_merge():
             "device merge of 8 shards")
 
 
+@pytest.mark.parametrize("kv", ["fp8_e4m3fn", "bf16"])
+def test_dcp_multi_token_verification(kv):
+    """DCP with T > 1 (several draft tokens verified under decode context parallelism):
+    each request's history split into 8 contiguous position shards, the T drafts being
+    the last T positions, so they sit in the last shard.  Every position of shards 0..6
+    precedes the drafts and is visible to every token (a non-causal call); the last
+    shard is a causal call on its local history.  The 8 shard answers, merged on the
+    host and with mla_merge_lse, equal the unsharded causal oracle."""
+    import dataclasses
+    import torch
+
+    B, T, H, ways = 2, 4, 48, 8
+    glob_lens = [8 * 520, 8 * 300 + 5]
+    rng = np.random.default_rng(302)
+    xs = [rng.standard_normal((L, 576), dtype=np.float32) for L in glob_lens]
+    if kv == "fp8_e4m3fn":
+        sigma = wk.e4m3fn_scale(max(float(np.abs(x).max()) for x in xs))
+        enc = [wk.to_e4m3fn_codes(x / sigma) for x in xs]
+        empty, dec = wk.E4M3FN_NAN, (lambda c: oracle.e4m3fn_codes_to_f64(c) * float(sigma))
+    else:
+        sigma = np.float32(1.0)
+        enc = [wk.to_bf16_bits(x) for x in xs]
+        empty, dec = wk.BF16_NAN, oracle.bf16_bits_to_f64
+    q_bits = wk.to_bf16_bits(rng.standard_normal((B, T, H, 576), dtype=np.float32))
+    o_parts, l_parts = [], []
+    for s in range(ways):
+        lo = [(L // ways) * s for L in glob_lens]
+        hi = [(L // ways) * (s + 1) if s < ways - 1 else L for L in glob_lens]
+        seq = np.array([h - l for l, h in zip(lo, hi)], dtype=np.int32)
+        pages = [-(-int(n) // 64) for n in seq]
+        table = np.full((B, max(pages)), -1, dtype=np.int32)
+        pool = np.full((sum(pages), 64, 576), empty, dtype=enc[0].dtype)
+        nxt = 0
+        for r in range(B):
+            table[r, :pages[r]] = np.arange(nxt, nxt + pages[r])
+            nxt += pages[r]
+            j = np.arange(seq[r])
+            pool[table[r, j // 64], j % 64] = enc[r][lo[r]:hi[r]]
+        wl = wk.Workload("dcp_shard_T4", 302, B, T, H, seq, kv, sigma, table, pool, q_bits,
+                         causal=s == ways - 1)
+        o, l = run_gpu(wl)
+        o_parts.append(o)
+        l_parts.append(l)
+    lat = [dec(e) for e in enc]
+    o_ref, l_ref = oracle.decode(oracle.bf16_bits_to_f64(q_bits), lat, wk.SOFTMAX_SCALE, causal=True)
+    o_host, l_host = oracle.merge(np.stack(o_parts), np.stack(l_parts))
+    wl = dataclasses.replace(wl, name="dcp_8_shards_T4")
+    compare(wl, o_host, l_host, o_ref, l_ref, "host merge of 8 shards, T = 4")
+    rows = B * T * H
+    po = torch.from_numpy(np.stack(o_parts).astype(np.float32)).to(torch.bfloat16).cuda()
+    pl = torch.from_numpy(np.stack(l_parts).astype(np.float32)).cuda()
+    out = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    mb.merge_lse(po.view(ways, rows, 512), pl.view(ways, rows), out=out, out_lse=lse)
+    torch.cuda.synchronize()
+    compare(wl, out.float().cpu().numpy().reshape(B, T, H, 512).astype(np.float64),
+            lse.cpu().numpy().reshape(B, T, H).astype(np.float64), o_ref, l_ref,
+            "device merge of 8 shards, T = 4")
+
+
 @pytest.mark.parametrize("P", [7, 32, 33, 300])
 def test_merge_lse_api(P):
     """Both merge shapes: up to 32 parts a row runs row-wise, more by column chunks."""
