@@ -183,7 +183,7 @@ def wk_elem(kv_format):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               f"multi-GPU path: run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
