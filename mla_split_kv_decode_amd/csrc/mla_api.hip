@@ -99,7 +99,7 @@ int wg_per_cu(bool fp8, int rbw) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.4 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.5 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 

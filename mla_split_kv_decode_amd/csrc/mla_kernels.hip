@@ -876,12 +876,15 @@ __device__ __forceinline__ void partial_ks(
       // bf16 kernel (mostly a few pages per piece) measured faster with the copy of page
       // i + kTiles issued after a barrier at the end of page i.
       constexpr bool kTopIssue = FP8 || RBW == 2;
-      // Parts of a top-issued copy: operations [0, kS1) at the top, [kS1, kS2) after the
-      // row-max barrier, the rest after the P^T barrier.  With four FP8 tiles a copy has
-      // three pages to land (2 + 2 + 1 of five); with two bf16 tiles it must land within
-      // the page, so two thirds go at the top and the rest after the row-max barrier
-      // (6 + 3 of nine; 5 + 4, 4 + 5, 3 + 3 + 3 and 7 + 2 measured slower).
-      constexpr int kS1 = kTiles >= 4 ? 2 : 6, kS2 = kTiles >= 4 ? 4 : kPer;
+      // Parts of a top-issued copy: operations [0, kS1) at the top, [kS1, kSm) after K
+      // read kMidRead of the QK^T phase (the copy engine drains them under the MFMAs),
+      // [kSm, kS2) after the row-max barrier, the rest after the P^T barrier.  With four
+      // FP8 tiles a copy has three pages to land (2 + 0 + 2 + 1 of five); with two bf16
+      // tiles it must land within the page: 3 + 3 + 3 of nine (6 + 3 at the top and after
+      // the row-max barrier 1.2% slower, 2 + 4 + 3 and 3 + 4 + 2 about as fast; 4 + 4 + 1,
+      // 5 + 3 + 1, 3 + 3 + 3 after the P^T barrier, and the splits that spill, slower).
+      constexpr int kS1 = kTiles >= 4 ? 2 : 3, kS2 = kTiles >= 4 ? 4 : kPer;
+      constexpr int kSm = kTiles >= 4 ? kS1 : 6, kMidRead = 5;
       int32_t next_id = kTopIssue ? page_id(kTiles) : 0;
       for (int i = 0; i < n; ++i) {
         // the pages issued after page i may stay in flight (top issue: kTiles - 1 of them
@@ -911,6 +914,9 @@ __device__ __forceinline__ void partial_ks(
               kt + OperandAddr<FP8>::kbase_of(lrow, lgrp, kk & 1, u) + OperandAddr<FP8>::kstep(kk);
           if constexpr (FP8) kf[s] = fp8x8_to_bf16x8(*(const i32x2*)ka);
           else kf[s] = *(const bf16x8*)ka;
+          if constexpr (kTopIssue && kSm > kS1) {
+            if (s == kMidRead && pc_go) copy.template part<kS1, kSm>(pc_base, pc_src, pc_valid);
+          }
         }
         f32x4 sp[RBW];
 #pragma unroll
@@ -1033,7 +1039,7 @@ __device__ __forceinline__ void partial_ks(
         }
         barrier_lds();
         if constexpr (kTopIssue) {
-          if (pc_go) copy.template part<kS1, kS2>(pc_base, pc_src, pc_valid);
+          if (pc_go) copy.template part<kSm, kS2>(pc_base, pc_src, pc_valid);
         }
 
         // ---- online softmax update; half 0 builds P^T of its sub-tile for every wave.  The
