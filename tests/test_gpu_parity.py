@@ -375,19 +375,27 @@ def test_dcp_shard_merge():
             "device merge of 8 shards")
 
 
-@pytest.mark.parametrize("kv", ["fp8_e4m3fn", "bf16"])
-def test_dcp_multi_token_verification(kv):
+@pytest.mark.parametrize("kv,split", [("fp8_e4m3fn", "contiguous"), ("bf16", "contiguous"),
+                                      ("fp8_e4m3fn", "pages"), ("bf16", "pages")])
+def test_dcp_multi_token_verification(kv, split):
     """DCP with T > 1 (several draft tokens verified under decode context parallelism):
-    each request's history split into 8 contiguous position shards, the T drafts being
-    the last T positions, so they sit in the last shard.  Every position of shards 0..6
-    precedes the drafts and is visible to every token (a non-causal call); the last
-    shard is a causal call on its local history.  The 8 shard answers, merged on the
-    host and with mla_merge_lse, equal the unsharded causal oracle."""
+    each request's history split into 8 position shards, contiguous ranges or pages dealt
+    round robin.  The T drafts are the last T positions; with these lengths they lie in
+    one page, so in one shard (the last range, or the owner of the last page), where they
+    are that shard's last T positions: it is a causal call on its local history.  Every
+    position of the other shards precedes the drafts and is visible to every token (a
+    non-causal call).  The 8 shard answers, merged on the host and with mla_merge_lse,
+    equal the unsharded causal oracle.  (Drafts that straddle two shards would need
+    per-token visible counts, which the shard call does not take.)"""
     import dataclasses
     import torch
 
     B, T, H, ways = 2, 4, 48, 8
-    glob_lens = [8 * 520, 8 * 300 + 5]
+    # 65 and 41 pages: both last pages go to shard 0 under the round robin (one causal
+    # flag serves a whole call, so the requests' drafts must share a shard)
+    glob_lens = [65 * 64, 40 * 64 + 5]
+    for L in glob_lens:
+        assert (L - T) // 64 == (L - 1) // 64  # the drafts share a page
     rng = np.random.default_rng(302)
     xs = [rng.standard_normal((L, 576), dtype=np.float32) for L in glob_lens]
     if kv == "fp8_e4m3fn":
@@ -400,11 +408,19 @@ def test_dcp_multi_token_verification(kv):
         empty, dec = wk.BF16_NAN, oracle.bf16_bits_to_f64
     q_bits = wk.to_bf16_bits(rng.standard_normal((B, T, H, 576), dtype=np.float32))
     o_parts, l_parts = [], []
+    def shard_positions(r, s):  # global positions held by shard s, in local order
+        L = glob_lens[r]
+        if split == "contiguous":
+            return np.arange((L // ways) * s, (L // ways) * (s + 1) if s < ways - 1 else L)
+        pos = np.arange(L)
+        return pos[(pos // 64) % ways == s]
+
     for s in range(ways):
-        lo = [(L // ways) * s for L in glob_lens]
-        hi = [(L // ways) * (s + 1) if s < ways - 1 else L for L in glob_lens]
-        seq = np.array([h - l for l, h in zip(lo, hi)], dtype=np.int32)
-        pages = [-(-int(n) // 64) for n in seq]
+        held = [shard_positions(r, s) for r in range(B)]
+        seq = np.array([len(h) for h in held], dtype=np.int32)
+        has_drafts = [len(h) > 0 and h[-1] == glob_lens[r] - 1 for r, h in enumerate(held)]
+        assert all(has_drafts) or not any(has_drafts)  # same shard for both requests here
+        pages = [max(1, -(-int(n) // 64)) for n in seq]
         table = np.full((B, max(pages)), -1, dtype=np.int32)
         pool = np.full((sum(pages), 64, 576), empty, dtype=enc[0].dtype)
         nxt = 0
@@ -412,9 +428,9 @@ def test_dcp_multi_token_verification(kv):
             table[r, :pages[r]] = np.arange(nxt, nxt + pages[r])
             nxt += pages[r]
             j = np.arange(seq[r])
-            pool[table[r, j // 64], j % 64] = enc[r][lo[r]:hi[r]]
+            pool[table[r, j // 64], j % 64] = enc[r][held[r]]
         wl = wk.Workload("dcp_shard_T4", 302, B, T, H, seq, kv, sigma, table, pool, q_bits,
-                         causal=s == ways - 1)
+                         causal=any(has_drafts))
         o, l = run_gpu(wl)
         o_parts.append(o)
         l_parts.append(l)
@@ -422,7 +438,7 @@ def test_dcp_multi_token_verification(kv):
     o_ref, l_ref = oracle.decode(oracle.bf16_bits_to_f64(q_bits), lat, wk.SOFTMAX_SCALE, causal=True)
     o_host, l_host = oracle.merge(np.stack(o_parts), np.stack(l_parts))
     wl = dataclasses.replace(wl, name="dcp_8_shards_T4")
-    compare(wl, o_host, l_host, o_ref, l_ref, "host merge of 8 shards, T = 4")
+    compare(wl, o_host, l_host, o_ref, l_ref, f"host merge of 8 {split} shards, T = 4")
     rows = B * T * H
     po = torch.from_numpy(np.stack(o_parts).astype(np.float32)).to(torch.bfloat16).cuda()
     pl = torch.from_numpy(np.stack(l_parts).astype(np.float32)).cuda()
@@ -432,7 +448,7 @@ def test_dcp_multi_token_verification(kv):
     torch.cuda.synchronize()
     compare(wl, out.float().cpu().numpy().reshape(B, T, H, 512).astype(np.float64),
             lse.cpu().numpy().reshape(B, T, H).astype(np.float64), o_ref, l_ref,
-            "device merge of 8 shards, T = 4")
+            f"device merge of 8 {split} shards, T = 4")
 
 
 @pytest.mark.parametrize("P", [7, 32, 33, 300])
