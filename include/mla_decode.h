@@ -143,7 +143,7 @@ typedef struct mla_plan mla_plan; /* opaque, host memory */
  * "What to optimise next": count the independent work so that all compute units
  * are busy).  A plan depends only on the shape, the host copy of seq_lens, the KV
  * dtype and the compute-unit count, so one plan serves every layer of a decode step.
- *   seq_lens_host  int32 [batch] host memory, each >= q_len
+ *   seq_lens_host  int32 [batch] host memory, each >= q_len with causal = 1, else >= 1
  *   page_size      must be MLA_PAGE_SIZE
  *   num_cus        compute units to fill; 0 = query the current device
  *   plan           out: new plan, release with mla_plan_destroy
@@ -174,6 +174,19 @@ int32_t mla_plan_row_groups(const mla_plan* plan);
  * (MLA_ERR_INVALID_ARGUMENT).
  */
 mla_status mla_plan_set_fp8_qk(mla_plan* plan, int32_t enable);
+/*
+ * Optional per-(request, token) visibility (Kimi K3 on MI355X, section 1 "Cache", DCP8
+ * paragraph, and the multi-token verification it extends to): hidden = device int32
+ * [batch][q_len], caller-owned, read by every later decode call with this plan (keep it
+ * alive and unchanged meanwhile).  Token t of request r then attends to the first
+ * seq_lens[r] - hidden[r][t] positions of its history (values below 0 count as 0; a
+ * value of seq_lens[r] or more hides everything: that row's partial answer is empty,
+ * LSE = -inf and O = 0).  This replaces the causal pattern (hidden = q_len - 1 - t), so
+ * a decode-context-parallel shard whose local history ends with some of the draft tokens
+ * can mask exactly the drafts each token may not see.  hidden = NULL restores the
+ * shape's causal flag.  Errors: plan NULL (MLA_ERR_INVALID_ARGUMENT).
+ */
+mla_status mla_plan_set_hidden(mla_plan* plan, const int32_t* hidden);
 /*
  * Host copy of the work list, for inspection: 5 int32 per piece
  * (workgroup, request, first page, end page (exclusive), partial slot), in workgroup

@@ -67,6 +67,7 @@ def _signatures():
         "mla_plan_num_parts": (c.c_int32, [P]),
         "mla_plan_row_groups": (c.c_int32, [P]),
         "mla_plan_set_fp8_qk": (c.c_int, [P, c.c_int32]),
+        "mla_plan_set_hidden": (c.c_int, [P, P]),
         "mla_plan_get_work": (c.c_int32, [P, P, c.c_int32]),
         "mla_decode_splitkv": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_size_t, P, c.c_int32,
                                          P, P]),
@@ -177,6 +178,14 @@ class Plan:
     @property
     def row_groups(self):
         return load().mla_plan_row_groups(self._h)
+
+    def set_hidden(self, hidden):
+        """Per-(request, token) hidden tails: int32 device tensor [batch][q_len] or None.
+        The tensor must stay alive while the plan is used."""
+        if hidden is not None:
+            assert tuple(hidden.shape) == (self.batch, self.q_len) and hidden.is_contiguous()
+        self._hidden = hidden  # keep it alive with the plan
+        _check(load().mla_plan_set_hidden(self._h, _ptr(hidden)))
 
     def set_fp8_qk(self, enable):
         """q.k on the FP8 matrix cores (FP8 pool, two or more 16-row blocks)."""

@@ -42,6 +42,7 @@ struct mla_plan {
   int32_t num_slots;     // partial answers the workspace holds
   int32_t part_bf16;     // partial O element type
   int32_t fp8_qk;        // QK^T on the FP8 matrix cores (mla_plan_set_fp8_qk)
+  const int32_t* hidden; // per-(request, token) hidden tails, device (mla_plan_set_hidden)
   int64_t total_pages;
   int32_t max_req_pages;  // largest ceil(seq_len / page) of a request
   int32_t max_req_slots;  // most partial answers of one request
@@ -99,7 +100,7 @@ int wg_per_cu(bool fp8, int rbw) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.5 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.6 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -167,8 +168,11 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   int64_t total_pages = 0;
   int32_t max_req_pages = 0;
   for (int32_t r = 0; r < s.batch; ++r) {
-    if (seq_lens_host[r] < s.q_len)
-      return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d < q_len %d", r, seq_lens_host[r], s.q_len);
+    // causal: the query tokens are the last q_len positions; otherwise (a context shard
+    // of a longer history) any non-empty history
+    const int32_t min_len = s.causal ? s.q_len : 1;
+    if (seq_lens_host[r] < min_len)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d < %d", r, seq_lens_host[r], min_len);
     const int32_t pg = pages_of(seq_lens_host[r], INT32_MAX);
     total_pages += pg;
     if (pg > max_req_pages) max_req_pages = pg;
@@ -260,6 +264,12 @@ int32_t mla_plan_num_units(const mla_plan* plan) { return plan ? plan->num_wg : 
 int32_t mla_plan_num_parts(const mla_plan* plan) { return plan ? plan->num_slots : -1; }
 
 int32_t mla_plan_row_groups(const mla_plan* plan) { return plan ? plan->row_groups : -1; }
+
+mla_status mla_plan_set_hidden(mla_plan* plan, const int32_t* hidden) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "null plan");
+  plan->hidden = hidden;
+  return ok();
+}
 
 mla_status mla_plan_set_fp8_qk(mla_plan* plan, int32_t enable) {
   if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "null plan");
@@ -376,6 +386,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   pp.score_scale = s.softmax_scale * log2e * (fp8 ? kv->kv_scale : 1.0f);
   pp.v_scale = fp8 ? kv->kv_scale : 1.0f;
   fill_plan_args(*plan, &pp.plan);
+  pp.hidden = plan->hidden;
   if (!out && !out_lse) {
     if (plan->num_wg > 0) {
       hipError_t e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);

@@ -123,6 +123,8 @@ struct PartialParams {
   float score_scale;  // softmax_scale * log2(e) * kv_scale: scores in log2 units
   float v_scale;      // kv_scale applied to the value rows (1 for bf16)
   PlanArgs plan;
+  const int32_t* hidden;  // null, or [B][T]: token t of request r does not see the last
+                          // hidden[r][t] positions (replaces the causal pattern)
 };
 
 // Launch parameters of the LSE merge kernel.

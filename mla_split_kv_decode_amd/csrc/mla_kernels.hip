@@ -518,7 +518,7 @@ __device__ __forceinline__ bool unit_of_block(int nwg, int rgroups, int64_t& w, 
   return w < nwg;
 }
 
-template <bool FP8, int RBW, bool RS, bool F8QK>
+template <bool FP8, int RBW, bool RS, bool F8QK, bool HID>
 __device__ __forceinline__ void partial_ks(
     const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -551,7 +551,7 @@ __device__ __forceinline__ void partial_ks(
   // this workgroup's row blocks: token, output row of this lane's head, causal lag
   // (an odd row-block count is padded with one row block that repeats the last real one
   // and stores nothing)
-  int orow[RBW], lag[RBW];
+  int orow[RBW], lag[RBW], tok[RBW];
   bool head_ok[RBW];
   const int rb_last = args.qlen * args.hgroups - 1;
 #pragma unroll
@@ -561,6 +561,7 @@ __device__ __forceinline__ void partial_ks(
     const int head = hg * kRowsPerBlock + lrow;
     head_ok[j] = head < args.heads && g * RBW + j <= rb_last;
     orow[j] = t * args.heads + head;
+    tok[j] = t;
     lag[j] = args.causal ? args.qlen - 1 - t : 0;  // token t sees positions < L - lag
   }
   int lag_max = 0;
@@ -576,6 +577,14 @@ __device__ __forceinline__ void partial_ks(
   const uint32_t pbuf_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, pbuf) - __builtin_offsetof(SM, tiles));
 
   auto run_piece = [&](int r, int pb, int pe, int64_t slot, int L) {
+    if constexpr (HID) {  // per-(request, token) hidden tails instead of the causal pattern
+      lag_max = 0;
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+        lag[j] = min(max(p.hidden[(int64_t)r * args.qlen + tok[j]], 0), L);
+        lag_max = max(lag_max, lag[j]);
+      }
+    }
     const int32_t* trow = block_table + (int64_t)r * args.maxp;
     const int n = pe - pb;
     bool bad = false;
@@ -1510,14 +1519,14 @@ static_assert(KSplitCfg<false, 1>::NW * 64 == kPartialThreads, "workgroup size")
 
 // Eight waves, two per SIMD; the page tiles cap residency at one workgroup per compute
 // unit, so each wave may hold up to 256 registers.
-template <bool FP8, int RBW, bool F8QK>
+template <bool FP8, int RBW, bool F8QK, bool HID>
 __global__ __launch_bounds__(kPartialThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     void* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ KSplitSmem<FP8, RBW> sm;
-  partial_ks<FP8, RBW, RBW == 2, F8QK>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+  partial_ks<FP8, RBW, RBW == 2, F8QK, HID>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1526,9 +1535,16 @@ namespace {
 
 template <bool FP8, int RBW, bool F8QK = false>
 hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK>), dim3(partial_grid(p.num_wg, p.row_groups)),
-                     dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
-                     p.seq_lens, p.part_o, p.part_lse);
+  // hidden tails get kernels of their own: the per-piece table read costs the plain
+  // kernels a few percent when compiled in
+  if (p.hidden)
+    hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, true>), dim3(partial_grid(p.num_wg, p.row_groups)),
+                       dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
+                       p.seq_lens, p.part_o, p.part_lse);
+  else
+    hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, false>), dim3(partial_grid(p.num_wg, p.row_groups)),
+                       dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
+                       p.seq_lens, p.part_o, p.part_lse);
   return hipGetLastError();
 }
 

@@ -90,7 +90,9 @@ def test_plan_argument_checks():
     assert plan_status(splits=-1) == E
     assert plan_status(page=32) == U
     assert plan_status(dtype=mb.MLA_FP32) == U
-    assert plan_status(q_len=4, seq_lens=(3,)) == E  # seq_len < q_len
+    assert plan_status(q_len=4, seq_lens=(3,)) == E  # causal: seq_len < q_len
+    assert plan_status(q_len=4, seq_lens=(3,), causal=0) == mb.MLA_OK  # a shard's history
+    assert plan_status(q_len=4, seq_lens=(0,), causal=0) == E
     assert plan_status(heads=129) == mb.MLA_OK  # 9 row blocks
     assert plan_status(q_len=3, heads=48, seq_lens=(100,)) == mb.MLA_OK  # 9 row blocks
     assert plan_status(q_len=8, heads=16, seq_lens=(100,)) == mb.MLA_OK
@@ -125,6 +127,16 @@ def test_fp8_qk_option_rules(dtype, q_len, heads, want):
     if want != mb.MLA_OK:
         with pytest.raises(mb.MlaError):
             mb.Plan(1, q_len, heads, [1000], TAU, kv_dtype=dtype, num_cus=256, fp8_qk=True)
+
+
+def test_hidden_tails_setter():
+    """mla_plan_set_hidden only records the caller's device pointer: any non-null plan
+    takes a pointer or NULL (which restores the causal pattern); a null plan is refused."""
+    lib = mb.load()
+    plan = mb.Plan(2, 4, 16, [1000, 700], TAU, num_cus=256)
+    assert lib.mla_plan_set_hidden(plan.handle, _fake(1 << 22)) == mb.MLA_OK
+    assert lib.mla_plan_set_hidden(plan.handle, None) == mb.MLA_OK
+    assert lib.mla_plan_set_hidden(None, None) == mb.MLA_ERR_INVALID_ARGUMENT
 
 
 def test_kv_append_argument_checks_enqueue_nothing():

@@ -34,7 +34,7 @@ def kv_dtype_of(wl):
 
 
 def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, heads=None,
-            block_table=None, pool=None, canary=False, partial="fp32", fp8_qk=False):
+            block_table=None, pool=None, canary=False, partial="fp32", fp8_qk=False, hidden=None):
     """Decode a workload on the GPU; returns (O fp64 [B][T][H][512], LSE fp64 [B][T][H])."""
     import torch
 
@@ -45,6 +45,8 @@ def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, head
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
                    causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype_of(wl),
                    partials_bf16=partial == "bf16", fp8_qk=fp8_qk)
+    if hidden is not None:
+        plan.set_hidden(torch.from_numpy(np.ascontiguousarray(hidden, dtype=np.int32)).cuda())
     ws = mb.workspace(plan)
     B, T, H = wl.batch, wl.q_len, wl.num_heads
     tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
@@ -449,6 +451,122 @@ def test_dcp_multi_token_verification(kv, split):
     compare(wl, out.float().cpu().numpy().reshape(B, T, H, 512).astype(np.float64),
             lse.cpu().numpy().reshape(B, T, H).astype(np.float64), o_ref, l_ref,
             f"device merge of 8 {split} shards, T = 4")
+
+
+@pytest.mark.parametrize("kv,split", [("bf16", "pages"), ("fp8_e4m3fn", "pages"),
+                                      ("bf16", "ragged"), ("fp8_e4m3fn", "ragged")])
+def test_dcp_straddling_drafts_with_hidden_tails(kv, split):
+    """DCP with T > 1 where the drafts straddle two shards and lie in different shards per
+    request.  Each shard call is non-causal with per-(request, token) hidden tails: token
+    t (global position L - T + t) does not see the held positions after it, which are the
+    last ones of the shard's local history.  A shard whose every held position is hidden
+    from a token returns an empty part (LSE = -inf) for it.  The 8 merged shard answers
+    equal the unsharded causal oracle."""
+    import dataclasses
+    import torch
+
+    B, T, H, ways = 2, 4, 48, 8
+    if split == "pages":  # drafts over pages 64|65 (shards 0, 1) and 39|40 (shards 7, 0)
+        glob_lens = [65 * 64 + 2, 40 * 64 + 1]
+    else:  # uneven contiguous ranges; the last shard holds only the last 2 positions
+        glob_lens = [3000, 1537]
+    rng = np.random.default_rng(305)
+    xs = [rng.standard_normal((L, 576), dtype=np.float32) for L in glob_lens]
+    if kv == "fp8_e4m3fn":
+        sigma = wk.e4m3fn_scale(max(float(np.abs(x).max()) for x in xs))
+        enc = [wk.to_e4m3fn_codes(x / sigma) for x in xs]
+        empty, dec = wk.E4M3FN_NAN, (lambda c: oracle.e4m3fn_codes_to_f64(c) * float(sigma))
+    else:
+        sigma = np.float32(1.0)
+        enc = [wk.to_bf16_bits(x) for x in xs]
+        empty, dec = wk.BF16_NAN, oracle.bf16_bits_to_f64
+    q_bits = wk.to_bf16_bits(rng.standard_normal((B, T, H, 576), dtype=np.float32))
+
+    def shard_positions(r, s):
+        L = glob_lens[r]
+        pos = np.arange(L)
+        if split == "pages":
+            return pos[(pos // 64) % ways == s]
+        cuts = np.concatenate([[0], np.sort(rng_cuts[r]), [L - 2, L]])
+        return pos[cuts[s]:cuts[s + 1]]
+
+    rng_cuts = [np.random.default_rng(306 + r).choice(np.arange(64, L - 64), ways - 2,
+                                                      replace=False) for r, L in enumerate(glob_lens)]
+    o_parts, l_parts, straddle = [], [], 0
+    for s in range(ways):
+        held = [shard_positions(r, s) for r in range(B)]
+        seq = np.array([len(h) for h in held], dtype=np.int32)
+        # token t of request r is at global position L - T + t and sees what precedes it
+        hidden = np.array([[int(np.sum(held[r] > glob_lens[r] - T + t)) for t in range(T)]
+                           for r in range(B)], dtype=np.int32)
+        straddle += int(np.any((hidden > 0) & (hidden < seq[:, None])))
+        pages = [max(1, -(-int(n) // 64)) for n in seq]
+        table = np.full((B, max(pages)), -1, dtype=np.int32)
+        pool = np.full((sum(pages), 64, 576), empty, dtype=enc[0].dtype)
+        nxt = 0
+        for r in range(B):
+            table[r, :pages[r]] = np.arange(nxt, nxt + pages[r])
+            nxt += pages[r]
+            j = np.arange(seq[r])
+            pool[table[r, j // 64], j % 64] = enc[r][held[r]]
+        wl = wk.Workload("dcp_shard_T4_hidden", 305, B, T, H, seq, kv, sigma, table, pool,
+                         q_bits, causal=False)
+        o, l = run_gpu(wl, hidden=hidden)
+        o_parts.append(o)
+        l_parts.append(l)
+    assert straddle >= 2  # more than one shard holds drafts
+    lat = [dec(e) for e in enc]
+    o_ref, l_ref = oracle.decode(oracle.bf16_bits_to_f64(q_bits), lat, wk.SOFTMAX_SCALE, causal=True)
+    o_host, l_host = oracle.merge(np.stack(o_parts), np.stack(l_parts))
+    wl = dataclasses.replace(wl, name="dcp_8_shards_T4_hidden")
+    compare(wl, o_host, l_host, o_ref, l_ref, f"host merge of 8 {split} shards, straddling drafts")
+    rows = B * T * H
+    po = torch.from_numpy(np.stack(o_parts).astype(np.float32)).to(torch.bfloat16).cuda()
+    pl = torch.from_numpy(np.stack(l_parts).astype(np.float32)).cuda()
+    out = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    mb.merge_lse(po.view(ways, rows, 512), pl.view(ways, rows), out=out, out_lse=lse)
+    torch.cuda.synchronize()
+    compare(wl, out.float().cpu().numpy().reshape(B, T, H, 512).astype(np.float64),
+            lse.cpu().numpy().reshape(B, T, H).astype(np.float64), o_ref, l_ref,
+            f"device merge of 8 {split} shards, straddling drafts")
+
+
+@pytest.mark.parametrize("B,T,H,kv", [(2, 4, 16, "bf16"), (2, 3, 48, "fp8_e4m3fn"),
+                                      (3, 2, 96, "fp8_e4m3fn"), (1, 4, 7, "bf16")])
+def test_hidden_tails_reproduce_causal_and_full(B, T, H, kv):
+    """Hidden tails q_len - 1 - t on a non-causal plan are the causal pattern, and zero
+    tails on a causal plan show every position: both bitwise equal to the plain calls."""
+    wl = wk.make_workload(None, seed=303, batch=B, q_len=T, num_heads=H,
+                          seq_lens=[700 + 97 * r for r in range(B)], kv_format=kv)
+    causal_tail = np.tile(np.arange(T - 1, -1, -1, dtype=np.int32), (B, 1))
+    o_c, l_c = run_gpu(dataclasses_replace(wl, causal=True))
+    o_h, l_h = run_gpu(dataclasses_replace(wl, causal=False), hidden=causal_tail)
+    assert np.array_equal(o_c, o_h) and np.array_equal(l_c, l_h)
+    o_n, l_n = run_gpu(dataclasses_replace(wl, causal=False))
+    o_z, l_z = run_gpu(dataclasses_replace(wl, causal=True), hidden=np.zeros((B, T), np.int32))
+    assert np.array_equal(o_n, o_z) and np.array_equal(l_n, l_z)
+    assert not np.array_equal(l_c, l_n)  # the two patterns do differ
+
+
+def test_hidden_tail_covering_the_history_gives_empty_rows():
+    wl = wk.make_workload(None, seed=304, batch=2, q_len=2, num_heads=16, seq_lens=[300, 500])
+    hidden = np.array([[0, 300], [-5, 499]], dtype=np.int32)  # (1, 1): everything hidden
+    o, l = run_gpu(wl, out_dtype="fp32", hidden=hidden)
+    assert np.all(np.isneginf(l[0, 1])) and np.all(o[0, 1] == 0)
+    o_ref, l_ref = run_oracle(dataclasses_replace(wl, causal=False))
+    compare(wl, o[0, 0], l[0, 0], o_ref[0, 0], l_ref[0, 0], "hidden 0")
+    compare(wl, o[1, 0], l[1, 0], o_ref[1, 0], l_ref[1, 0], "negative hidden counts as 0")
+    # hiding 499 of 500 leaves position 0 alone: O is its value row, LSE its scaled score
+    one = dataclasses_replace(wl, seq_lens=np.array([300, 1], dtype=np.int32), causal=False)
+    o1, l1 = run_oracle(one, requests=[1])
+    compare(wl, o[1:2, 1:2], l[1:2, 1:2], o1[:, 1:2], l1[:, 1:2], "one visible position")
+
+
+def dataclasses_replace(wl, **kw):
+    import dataclasses
+
+    return dataclasses.replace(wl, **kw)
 
 
 @pytest.mark.parametrize("P", [7, 32, 33, 300])
