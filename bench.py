@@ -35,12 +35,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # rocprofv3 FETCH_SIZE / WRITE_SIZE of the partial kernel (KiB per dispatch, median) and
 # the copy-kernel calibration factors (profiles/<kernel>_<workload>.md), keyed by
 # (workload, splits, partial storage, library version): a kernel change bumps the
-# version, so `traffic` reads null until the counters are taken again.  These were taken
-# at 0.6.4; 0.6.5 and 0.6.6 leave this kernel's instructions as they were (0.6.6 moves
-# only the offsets of its arguments), checked on the compiler's assembly.
+# version, so `traffic` reads null until the counters are taken again.
 TRAFFIC = {
     ("long32k", 0, "fp32", "mla_split_kv_decode_amd 0.6.6 (gfx950)"):
-        {"fetch_kib": 18589.5, "write_kib": 6240.0, "fetch_factor": 2.0, "write_factor": 1.0},
+        {"fetch_kib": 18587.0, "write_kib": 6240.0, "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
 

@@ -532,19 +532,22 @@ def test_dcp_straddling_drafts_with_hidden_tails(kv, split):
             f"device merge of 8 {split} shards, straddling drafts")
 
 
-@pytest.mark.parametrize("B,T,H,kv", [(2, 4, 16, "bf16"), (2, 3, 48, "fp8_e4m3fn"),
-                                      (3, 2, 96, "fp8_e4m3fn"), (1, 4, 7, "bf16")])
-def test_hidden_tails_reproduce_causal_and_full(B, T, H, kv):
+@pytest.mark.parametrize("B,T,H,kv,f8qk", [(2, 4, 16, "bf16", False), (2, 3, 48, "fp8_e4m3fn", False),
+                                           (3, 2, 96, "fp8_e4m3fn", False), (1, 4, 7, "bf16", False),
+                                           (2, 3, 48, "fp8_e4m3fn", True)])
+def test_hidden_tails_reproduce_causal_and_full(B, T, H, kv, f8qk):
     """Hidden tails q_len - 1 - t on a non-causal plan are the causal pattern, and zero
-    tails on a causal plan show every position: both bitwise equal to the plain calls."""
+    tails on a causal plan show every position: both bitwise equal to the plain calls
+    (also with QK^T on the FP8 matrix cores)."""
     wl = wk.make_workload(None, seed=303, batch=B, q_len=T, num_heads=H,
                           seq_lens=[700 + 97 * r for r in range(B)], kv_format=kv)
     causal_tail = np.tile(np.arange(T - 1, -1, -1, dtype=np.int32), (B, 1))
-    o_c, l_c = run_gpu(dataclasses_replace(wl, causal=True))
-    o_h, l_h = run_gpu(dataclasses_replace(wl, causal=False), hidden=causal_tail)
+    o_c, l_c = run_gpu(dataclasses_replace(wl, causal=True), fp8_qk=f8qk)
+    o_h, l_h = run_gpu(dataclasses_replace(wl, causal=False), hidden=causal_tail, fp8_qk=f8qk)
     assert np.array_equal(o_c, o_h) and np.array_equal(l_c, l_h)
-    o_n, l_n = run_gpu(dataclasses_replace(wl, causal=False))
-    o_z, l_z = run_gpu(dataclasses_replace(wl, causal=True), hidden=np.zeros((B, T), np.int32))
+    o_n, l_n = run_gpu(dataclasses_replace(wl, causal=False), fp8_qk=f8qk)
+    o_z, l_z = run_gpu(dataclasses_replace(wl, causal=True), hidden=np.zeros((B, T), np.int32),
+                       fp8_qk=f8qk)
     assert np.array_equal(o_n, o_z) and np.array_equal(l_n, l_z)
     assert not np.array_equal(l_c, l_n)  # the two patterns do differ
 
