@@ -183,7 +183,12 @@ class Plan:
         """Per-(request, token) hidden tails: int32 device tensor [batch][q_len] or None.
         The tensor must stay alive while the plan is used."""
         if hidden is not None:
-            assert tuple(hidden.shape) == (self.batch, self.q_len) and hidden.is_contiguous()
+            import torch
+
+            if (tuple(hidden.shape) != (self.batch, self.q_len) or hidden.dtype != torch.int32
+                    or not hidden.is_cuda or not hidden.is_contiguous()):
+                raise ValueError("hidden must be a contiguous int32 device tensor "
+                                 f"[{self.batch}][{self.q_len}]")
         self._hidden = hidden  # keep it alive with the plan
         _check(load().mla_plan_set_hidden(self._h, _ptr(hidden)))
 

@@ -137,6 +137,13 @@ def test_hidden_tails_setter():
     assert lib.mla_plan_set_hidden(plan.handle, _fake(1 << 22)) == mb.MLA_OK
     assert lib.mla_plan_set_hidden(plan.handle, None) == mb.MLA_OK
     assert lib.mla_plan_set_hidden(None, None) == mb.MLA_ERR_INVALID_ARGUMENT
+    import torch
+
+    with pytest.raises(ValueError):  # host memory is refused before the library sees it
+        plan.set_hidden(torch.zeros((2, 4), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        plan.set_hidden(torch.zeros((4, 2), dtype=torch.int32))
+    plan.set_hidden(None)
 
 
 def test_kv_append_argument_checks_enqueue_nothing():
