@@ -37,8 +37,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # (workload, splits, partial storage, library version): a kernel change bumps the
 # version, so `traffic` reads null until the counters are taken again.
 TRAFFIC = {
-    ("long32k", 0, "fp32", "mla_split_kv_decode_amd 0.6.6 (gfx950)"):
-        {"fetch_kib": 18587.0, "write_kib": 6240.0, "fetch_factor": 2.0, "write_factor": 1.0},
+    ("long32k", 0, "fp32", "mla_split_kv_decode_amd 0.6.7 (gfx950)"):
+        {"fetch_kib": 18593.0, "write_kib": 8924.1875, "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
 

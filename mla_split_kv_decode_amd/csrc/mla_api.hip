@@ -16,6 +16,7 @@
 
 namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, bool fp8_qk, hipStream_t stream);
+bool partial_nt_parts(bool part_bf16, int64_t max_row_slots);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
                         int max_row_slots, hipStream_t stream);
 size_t partial_lds_size(bool fp8, int rbw);
@@ -100,7 +101,7 @@ int wg_per_cu(bool fp8, int rbw) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.6 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.7 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -387,6 +388,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   pp.v_scale = fp8 ? kv->kv_scale : 1.0f;
   fill_plan_args(*plan, &pp.plan);
   pp.hidden = plan->hidden;
+  pp.nt_parts = partial_nt_parts(plan->part_bf16 != 0, plan->max_req_slots);
   if (!out && !out_lse) {
     if (plan->num_wg > 0) {
       hipError_t e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);

@@ -125,6 +125,7 @@ struct PartialParams {
   PlanArgs plan;
   const int32_t* hidden;  // null, or [B][T]: token t of request r does not see the last
                           // hidden[r][t] positions (replaces the causal pattern)
+  int32_t nt_parts;       // fp32 parts stored non-temporal (read by the column-chunk merge)
 };
 
 // Launch parameters of the LSE merge kernel.

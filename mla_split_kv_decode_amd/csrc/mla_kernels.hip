@@ -446,12 +446,18 @@ __device__ __forceinline__ void for_each_piece(const PartialParams& p, const Hot
 }
 
 // Partial answer of one row of one piece to the workspace layout of mla_internal.h:
-// four consecutive columns starting at `col`.
+// four consecutive columns starting at `col`.  NT: fp32 parts stored non-temporal, for
+// plans whose parts the column-chunk merge reads (more than kRowSlots a row): the
+// partial kernel ends sooner (long32k: 0.4 us of 11.6), while the row-wise merge, which
+// reads few parts a row, lost more on such parts than its partial kernel saved
+template <bool NT>
 __device__ __forceinline__ void store_partial(void* part_o, bool bf16, int64_t orow, int col,
                                               int nslots, int64_t slot, f32x4 v) {
   const int64_t idx = ((orow * kMergeChunks + (col >> 5)) * nslots + slot) * kMergeCols + (col & 31);
   if (bf16)
     *(bf16x4*)((__bf16*)part_o + idx) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  else if constexpr (NT)
+    __builtin_nontemporal_store(v, (f32x4*)((float*)part_o + idx));
   else
     *(f32x4*)((float*)part_o + idx) = v;
 }
@@ -518,7 +524,7 @@ __device__ __forceinline__ bool unit_of_block(int nwg, int rgroups, int64_t& w, 
   return w < nwg;
 }
 
-template <bool FP8, int RBW, bool RS, bool F8QK, bool HID>
+template <bool FP8, int RBW, bool RS, bool F8QK, bool HID, bool NT>
 __device__ __forceinline__ void partial_ks(
     const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -1154,7 +1160,7 @@ __device__ __forceinline__ void partial_ks(
       if (head_ok[j]) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
-          store_partial(part_o, args.pbf16, orow[j], 64 * wave + 16 * ct + 4 * lgrp, args.nslots, slot,
+          store_partial<NT>(part_o, args.pbf16, orow[j], 64 * wave + 16 * ct + 4 * lgrp, args.nslots, slot,
                         acc[j][ct] * oscale);
         if (wave == 0 && lgrp == 0) part_lse[(int64_t)orow[j] * args.nslots + slot] = lse;
       }
@@ -1519,32 +1525,36 @@ static_assert(KSplitCfg<false, 1>::NW * 64 == kPartialThreads, "workgroup size")
 
 // Eight waves, two per SIMD; the page tiles cap residency at one workgroup per compute
 // unit, so each wave may hold up to 256 registers.
-template <bool FP8, int RBW, bool F8QK, bool HID>
+template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
 __global__ __launch_bounds__(kPartialThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     void* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ KSplitSmem<FP8, RBW> sm;
-  partial_ks<FP8, RBW, RBW == 2, F8QK, HID>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+  partial_ks<FP8, RBW, RBW == 2, F8QK, HID, NT>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
 // ------------------------------------------------------------------ launchers
 
 namespace {
 
+template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
+void launch_partial_k(const PartialParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, HID, NT>), dim3(partial_grid(p.num_wg, p.row_groups)),
+                     dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
+                     p.seq_lens, p.part_o, p.part_lse);
+}
+
 template <bool FP8, int RBW, bool F8QK = false>
 hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
-  // hidden tails get kernels of their own: the per-piece table read costs the plain
-  // kernels a few percent when compiled in
-  if (p.hidden)
-    hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, true>), dim3(partial_grid(p.num_wg, p.row_groups)),
-                       dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
-                       p.seq_lens, p.part_o, p.part_lse);
-  else
-    hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, false>), dim3(partial_grid(p.num_wg, p.row_groups)),
-                       dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
-                       p.seq_lens, p.part_o, p.part_lse);
+  // hidden tails get kernels of their own (the per-piece table read costs the plain
+  // kernels a few percent when compiled in); non-temporal part stores only in the
+  // one-row-block kernel (the multi-row plans are merged row-wise)
+  const bool nt = RBW == 1 && p.nt_parts && !p.hidden;
+  if (p.hidden) launch_partial_k<FP8, RBW, F8QK, true, false>(p, stream);
+  else if (nt) launch_partial_k<FP8, RBW, F8QK, false, RBW == 1>(p, stream);
+  else launch_partial_k<FP8, RBW, F8QK, false, false>(p, stream);
   return hipGetLastError();
 }
 
@@ -1582,6 +1592,10 @@ hipError_t launch_kv_append(void* pool, int64_t num_pages, bool fp8, const int32
                        (uint8_t*)pool, num_pages, block_table, max_pages, seq_lens,
                        (const uint16_t*)latents, q_len, kv_scale);
   return hipGetLastError();
+}
+
+bool partial_nt_parts(bool part_bf16, int64_t max_row_slots) {
+  return !part_bf16 && max_row_slots > kRowSlots;
 }
 
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
