@@ -124,6 +124,9 @@ SMALL = [
     (2, 2, 96, [300, 100], 0, "bf16"),
     (2, 2, 96, [300, 100], 3, "fp8_e4m3fn"),
     (1, 4, 256, [130], 0, "bf16"),
+    # more than 32 parts a row: the column-chunk merge, fp32 parts stored non-temporal
+    (1, 1, 16, [4000], 0, "fp8_e4m3fn"),
+    (2, 1, 12, [4000, 2500], 0, "bf16"),
 ]
 
 
