@@ -30,10 +30,27 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TAU = float(np.float32(1.0 / math.sqrt(192.0)))
 
 
+def torch_bf16_to_f64(bits):
+    """bf16 bit patterns -> fp64 through torch's own bfloat16 type (independent of the
+    oracle's decoder)."""
+    import torch
+
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def torch_e4m3fn_to_f64(codes):
+    """E4M3FN codes -> fp64 through torch's float8_e4m3fn type."""
+    import torch
+
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    return torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
 def bf16_values(rng, shape, scale=1.0):
     """Random values exactly representable in bf16 (via the generator's cast)."""
     bits = wk.to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * scale)
-    return oracle.bf16_bits_to_f64(bits)
+    return torch_bf16_to_f64(bits)
 
 
 # ------------------------------------------------------------------ P1 decimal
@@ -43,7 +60,8 @@ def decimal_attention(q_rows, x, tau, prec=50):
     ctx = decimal.Context(prec=prec)
     D = decimal.Decimal
     tau_d = D(tau)
-    xs = [[D(float(v)) for v in row] for row in x]
+    # rows of x may be given as Decimals already (exact products such as code x scale)
+    xs = [[v if isinstance(v, D) else D(float(v)) for v in row] for row in x]
     outs, lses = [], []
     for q in q_rows:
         qd = [D(float(v)) for v in q]
@@ -79,26 +97,101 @@ def test_decimal_brute_force():
 def decimal_decode_paged(wl, r, t, h):
     """One output row of a paged workload, with the causal reading written out
     independently of the oracle (token t of T sees the first L - T + t + 1
-    positions) and every position gathered one by one."""
+    positions), every position gathered one by one, and the stored values decoded by
+    torch's bfloat16 / float8_e4m3fn types.  An FP8 value is its code's value times the
+    per-tensor scale, formed here in exact decimal arithmetic (Kimi K3 on MI355X,
+    section 1 "Cache": the latents are stored in FP8)."""
     L = int(wl.seq_lens[r])
     n = L - wl.q_len + t + 1
     rows = []
     for j in range(n):
         page = int(wl.block_table[r][j // wl.page_size])
-        rows.append(oracle.bf16_bits_to_f64(wl.pool[page, j % wl.page_size]))
-    q = oracle.bf16_bits_to_f64(wl.q_bits[r, t, h])[None]
-    return decimal_attention(q, np.array(rows), float(wl.softmax_scale), prec=40)
+        raw = wl.pool[page, j % wl.page_size]
+        if wl.kv_format == "bf16":
+            rows.append([decimal.Decimal(float(v)) for v in torch_bf16_to_f64(raw)])
+        else:
+            sigma = decimal.Decimal(float(np.float32(wl.kv_scale)))
+            rows.append([decimal.Decimal(float(v)) * sigma for v in torch_e4m3fn_to_f64(raw)])
+    q = torch_bf16_to_f64(wl.q_bits[r, t, h])[None]
+    return decimal_attention(q, rows, float(wl.softmax_scale), prec=40)
+
+
+def pin_decimal_paged(decode_paged_fn, kv_format, seed=5):
+    """Largest difference between decode_paged_fn and the decimal brute force on a small
+    shuffled paged workload with a causal two-token verify."""
+    wl = wk.make_workload(None, seed=seed, batch=2, q_len=2, num_heads=3, seq_lens=[70, 5],
+                          kv_format=kv_format, shuffled=True)
+    o, lse = decode_paged_fn(wl.q_bits, wl.pool, kv_format, wl.kv_scale, wl.block_table,
+                             wl.seq_lens, wl.page_size, wl.softmax_scale, causal=True)
+    worst = 0.0
+    for r, t, h in [(0, 0, 0), (0, 1, 2), (1, 0, 1), (1, 1, 0)]:
+        od, lsed = decimal_decode_paged(wl, r, t, h)
+        worst = max(worst, float(np.abs(o[r, t, h] - od[0]).max()), abs(float(lse[r, t, h] - lsed[0])))
+    return worst
 
 
 def test_decimal_paged_decode():
-    wl = wk.make_workload(None, seed=5, batch=2, q_len=2, num_heads=3, seq_lens=[70, 5],
-                          kv_format="bf16", shuffled=True)
-    o, lse = oracle.decode_paged(wl.q_bits, wl.pool, "bf16", 1.0, wl.block_table, wl.seq_lens,
-                                 wl.page_size, wl.softmax_scale, causal=True)
-    for r, t, h in [(0, 0, 0), (0, 1, 2), (1, 0, 1), (1, 1, 0)]:
-        od, lsed = decimal_decode_paged(wl, r, t, h)
-        assert np.abs(o[r, t, h] - od[0]).max() <= 1e-12
-        assert abs(lse[r, t, h] - lsed[0]) <= 1e-12
+    assert pin_decimal_paged(oracle.decode_paged, "bf16") <= 1e-12
+
+
+def test_decimal_paged_decode_fp8():
+    """FP8 pool: the oracle's codes x scale against decimal codes x scale, the codes
+    decoded by torch's float8_e4m3fn (the scale of this workload is about 1/100, so a
+    division in place of the product, or a dropped scale, is far off)."""
+    wl = wk.make_workload(None, seed=5, batch=1, q_len=1, num_heads=1, seq_lens=[3],
+                          kv_format="fp8_e4m3fn")
+    assert 1e-3 < float(wl.kv_scale) < 0.1
+    assert pin_decimal_paged(oracle.decode_paged, "fp8_e4m3fn") <= 1e-12
+
+
+def test_fp8_scale_mutants_fail(monkeypatch):
+    """Planted in the oracle: the FP8 rows divided by the scale, or the scale dropped."""
+    import importlib
+
+    att = importlib.import_module("oracle.attention")  # the module (the package re-exports a function of that name)
+    good = att.decode_latent_rows
+    for mutant in (lambda raw, fmt, sc: good(raw, fmt, 1.0) / float(np.float32(sc)) if fmt != "bf16"
+                   else good(raw, fmt, sc),
+                   lambda raw, fmt, sc: good(raw, fmt, 1.0) if fmt != "bf16" else good(raw, fmt, sc)):
+        monkeypatch.setattr(att, "decode_latent_rows", mutant)
+        assert pin_decimal_paged(att.decode_paged, "fp8_e4m3fn") > 1e-3
+        assert pin_decimal_paged(att.decode_paged, "bf16") <= 1e-12
+    monkeypatch.setattr(att, "decode_latent_rows", good)
+    assert pin_decimal_paged(att.decode_paged, "fp8_e4m3fn") <= 1e-12
+
+
+def pin_bf16_decoder(decode_fn):
+    """Number of the 65,536 bf16 bit patterns that decode_fn gets wrong against torch's
+    bfloat16 -> float64 conversion (NaN patterns must give NaN; the sign of zero counts)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = np.asarray(decode_fn(bits), dtype=np.float64)
+    ref = torch_bf16_to_f64(bits)
+    nan_ok = np.isnan(mine) == np.isnan(ref)
+    val_ok = np.isnan(ref) | ((mine == ref) & (np.signbit(mine) == np.signbit(ref)))
+    return int(np.sum(~(nan_ok & val_ok)))
+
+
+def test_bf16_decoder_all_patterns():
+    assert pin_bf16_decoder(oracle.bf16_bits_to_f64) == 0
+    # a few values written out from the format: sign, 8 exponent bits (bias 127), 7 mantissa bits
+    v = oracle.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x8000, 0x7F80],
+                                         dtype=np.uint16))
+    assert list(v[:4]) == [1.0, -2.0, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127]
+    assert v[4] == 0.0 and np.signbit(v[4]) and v[5] == np.inf
+
+
+def test_bf16_decoder_mutants_fail():
+    def shift15(bits):
+        return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+
+    def as_fp16(bits):
+        return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+    def byte_swapped(bits):
+        return oracle.bf16_bits_to_f64(np.asarray(bits, np.uint16).byteswap())
+
+    for fn in (shift15, as_fp16, byte_swapped):
+        assert pin_bf16_decoder(fn) > 1000
 
 
 # ------------------------------------------------------------- P2 closed forms
