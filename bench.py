@@ -1,8 +1,9 @@
 """Benchmark of the MLA split-KV decode hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long32k]
-                    [--splits auto|N] [--layers 24] [--mode graph|eager]
-                    [--no-cpu-baseline]
+                    [--splits auto|N] [--layers 24] [--repeats R]
+                    [--no-cpu-baseline] [--no-other-workloads]
+    python bench.py --read-ceiling [--workload long32k]
 
 A step is one MLA layer-step: the partial-attention kernel plus the LSE merge kernel
 for the whole batch of one layer, on one stream.  Consecutive steps rotate through
@@ -10,11 +11,20 @@ for the whole batch of one layer, on one stream.  Consecutive steps rotate throu
 MI355X, "Inside Kimi K3"), so the KV stream comes from HBM and not from the 256 MB
 memory-side cache.  Inputs are synthetic and already resident in HBM.
 
-The single JSON line reports KV-read GB/s (algorithmic KV bytes / time per layer-step,
-each cached latent read once) and the time per layer-step; `roofline` prices the
-partial kernel (the dominant one) against the 8 TB/s HBM peak, with its average
-duration measured here with HIP events on the stream it runs on; `cpu_baseline` times
-the fp64 oracle on a bounded sample of the same workload on the host cores.
+Timing: W untimed warm-up layer-steps, then R repeats of exactly K layer-steps, each
+repeat one replay of a graph holding the K steps, bracketed by HIP events on the launch
+stream; a device-side sleep queued before the first event keeps the host's launch of
+the replay out of the timed region.  The reported time is the median repeat / K.
+
+The JSON line reports KV-read GB/s (algorithmic KV bytes / time per layer-step, each
+cached latent read once) and the time per layer-step.  `roofline` prices the partial
+kernel (the dominant one), timed the same way on partial-only steps, against the 8 TB/s
+HBM peak, or against the 2.5 PFLOP/s dense bf16 matrix peak for a workload whose
+arithmetic intensity is past the ridge (the 96-head DCP shard).  `cpu_baseline` times
+the fp64 oracle on a bounded sample of the same workload on all host cores and on one
+thread.  `detail.workloads` holds a compact line for each other named workload (pools
+drawn on the device), and `--read-ceiling` times a plain read of the same rotated pools
+(the floor of any single launch that streams them) and an empty launch.
 """
 
 import argparse
@@ -31,31 +41,29 @@ sys.path.insert(0, REPO)
 METRIC = "MLA decode KV-read GB/s (% of 8 TB/s) and µs/layer-step at 32K ctx"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312.5
 
 # rocprofv3 FETCH_SIZE / WRITE_SIZE of the partial kernel (KiB per dispatch, median) and
 # the copy-kernel calibration factors (profiles/<kernel>_<workload>.md), keyed by
-# (workload, splits, partial storage, library version): a kernel change bumps the
-# version, so `traffic` reads null until the counters are taken again.
-TRAFFIC = {
-    ("long32k", 0, "fp32", "mla_split_kv_decode_amd 0.6.7 (gfx950)"):
-        {"fetch_kib": 18593.0, "write_kib": 8924.1875, "fetch_factor": 2.0, "write_factor": 1.0},
-}
+# (workload, splits, library version): a kernel change bumps the version, so `traffic`
+# reads null until the counters are taken again.
+TRAFFIC = {}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2400)
-    ap.add_argument("--warmup", type=int, default=240)
+    ap.add_argument("--steps", type=int, default=480, help="layer-steps timed per repeat")
+    ap.add_argument("--warmup", type=int, default=48, help="untimed layer-steps first")
+    ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--workload", default="long32k")
     ap.add_argument("--splits", default="auto")
-    ap.add_argument("--partial", default="fp32", choices=["bf16", "fp32"],
-                    help="storage type of the partial answers between the two kernels")
     ap.add_argument("--layers", type=int, default=24)
-    ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
-    ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="seconds of oracle work on all host cores (half that again on one thread)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the compact lines of the other named workloads")
     ap.add_argument("--q-len", type=int, default=0,
                     help="query tokens per request (draft depth of a verification step): the "
                          "workload's history prefix is kept and the T new tokens added to it")
@@ -64,6 +72,9 @@ def parse():
                          "of the decode, alone and followed by the decode")
     ap.add_argument("--fp8-qk", action="store_true",
                     help="q.k on the FP8 matrix cores (FP8 pool, two or more 16-row blocks)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="time a plain read of the workload's rotated pools (registers and LDS "
+                         "copies) and an empty launch, instead of the decode")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -91,27 +102,64 @@ def describe(wl, splits):
             f"{'auto' if splits == 0 else splits} splits")
 
 
+def time_steps(step, steps, warmup, repeats, nl):
+    """Median ms per layer-step over `repeats` replays of a graph of exactly `steps`
+    layer-steps (layer i % nl), after `warmup` eager layer-steps and one untimed replay."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i % nl)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i % nl)
+    g.replay()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(8_000_000)  # the GPU is busy while the replay is queued behind e0
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        res.append(e0.elapsed_time(e1) / steps)
+    del g
+    return res
+
+
 def cpu_baseline(wl, seconds):
     """The fp64 oracle, untuned, on the host: full layer-steps of the same workload
-    (all requests and heads) repeated for about `seconds`."""
+    (all requests and heads) repeated for about `seconds` on all cores, then for about
+    half that on one thread."""
     import oracle
     from mla_split_kv_decode_amd import workloads as wk
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl is installed in the image
+        threadpool_info, threadpool_limits = None, None
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_paged(wl.q_bits, wl.pool, wl.kv_format, wl.kv_scale, wl.block_table,
-                            wl.seq_lens, wl.page_size, wl.softmax_scale, causal=wl.causal)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / n
+    def run(limit_s):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.decode_paged(wl.q_bits, wl.pool, wl.kv_format, wl.kv_scale, wl.block_table,
+                                wl.seq_lens, wl.page_size, wl.softmax_scale, causal=wl.causal)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= limit_s:
+                return n, el / n
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1]) if threadpool_info else 0
+    n, per = run(seconds)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n1, per1 = run(seconds / 2)
+        one = {"value": round(wk.kv_bytes(wl.seq_lens, wl.kv_format) / per1 / 1e9, 4), "unit": "GB/s",
+               "cores": 1, "ms_per_step": round(per1 * 1e3, 3),
+               "sample": f"{n1} full layer-steps of {wl.name} on one BLAS thread"}
     return {
         "value": round(wk.kv_bytes(wl.seq_lens, wl.kv_format) / per / 1e9, 4),
         "unit": "GB/s",
@@ -120,51 +168,162 @@ def cpu_baseline(wl, seconds):
         "sample": f"{n} full layer-steps of {wl.name} (all requests and heads), "
                   f"{per * 1e3:.1f} ms each, {len(os.sched_getaffinity(0))} host cores visible",
         "ms_per_step": round(per * 1e3, 3),
+        "one_thread": one,
     }
 
 
-def bench_append(args, wl, mb, pools, scales, dev0, kv_dtype, decode_step, nl):
+def roofline_of(kv_b, flops, part_ms, traffic):
+    """The partial kernel against the roofline its arithmetic intensity puts it under."""
+    if flops / kv_b > RIDGE_FLOP_PER_BYTE:
+        achieved = flops / (part_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "mla_partial_kernel",
+                "kernel_us": round(part_ms * 1e3, 3), "flops_per_launch": int(flops),
+                "bytes_per_launch": int(kv_b),
+                "hbm_frac": round(kv_b / (part_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    achieved = kv_b / (part_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "mla_partial_kernel", "kernel_us": round(part_ms * 1e3, 3),
+            "bytes_per_launch": int(kv_b)}
+
+
+def setup(mb, wk, wl, splits, nl, fp8_qk=False, device_pools=False):
+    """Plan, workspace, outputs and the rotated pools' descriptors of a workload."""
+    import torch
+
+    kv_dtype = mb.MLA_BF16 if wl.kv_format == "bf16" else mb.MLA_FP8_E4M3FN
+    q = torch.from_numpy(wl.q_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    bt = torch.from_numpy(np.ascontiguousarray(wl.block_table)).cuda()
+    sl = torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).cuda()
+    if device_pools:
+        pools = wk.device_pools(wl, nl, wl.seed)
+    else:
+        pools = []
+        for layer in range(nl):
+            pool, sc = (wl.pool, wl.kv_scale) if layer == 0 else wk.layer_pool(wl, layer)
+            t = torch.from_numpy(pool.view(np.int16) if wl.kv_format == "bf16" else pool).cuda()
+            pools.append((t.view(torch.bfloat16) if wl.kv_format == "bf16" else t, float(sc)))
+    t0 = time.perf_counter()
+    plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
+                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype, fp8_qk=fp8_qk)
+    t_plan = time.perf_counter() - t0
+    ws = mb.workspace(plan)
+    B, T, H = wl.batch, wl.q_len, wl.num_heads
+    out = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+    kvs = [mb.paged_kv(p, bt, sl, kv_dtype, s) for p, s in pools]
+
+    def step(i, full=True):
+        mb.decode_splitkv(plan, q, kvs[i], ws, out=out if full else None,
+                          out_dtype=mb.MLA_BF16, out_lse=lse if full else None)
+
+    return dict(plan=plan, step=step, pools=pools, kvs=kvs, kv_dtype=kv_dtype, q=q, bt=bt, sl=sl,
+                t_plan=t_plan)
+
+
+def measure(args, mb, wk, wl, splits, nl, fp8_qk=False, device_pools=False, steps=None, warmup=None):
+    """Layer-step and partial-only timings of one workload."""
+    import torch
+
+    st = setup(mb, wk, wl, splits, nl, fp8_qk, device_pools)
+    step = st["step"]
+    step(0)  # first call outside any capture
+    torch.cuda.synchronize()
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    full = time_steps(lambda i: step(i, True), steps, warmup, args.repeats, nl)
+    part = time_steps(lambda i: step(i, False), steps, warmup, args.repeats, nl)
+    plan = st["plan"]
+    res = dict(full=full, part=part, ms=float(np.median(full)), ms_part=float(np.median(part)),
+               units=plan.num_units, row_groups=plan.row_groups, parts=plan.num_parts,
+               t_plan=st["t_plan"], steps=steps, warmup=warmup)
+    del st
+    torch.cuda.synchronize()
+    return res
+
+
+def compact_line(wl, splits, m):
+    kv_b = wk_kv_bytes(wl)
+    flops = wk_flops(wl)
+    return {
+        "workload": describe(wl, splits),
+        "us_per_layer_step": round(m["ms"] * 1e3, 3),
+        "GBps": round(kv_b / (m["ms"] * 1e-3) / 1e9, 2),
+        "pct_of_8TBs": round(100 * kv_b / (m["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "partial_us": round(m["ms_part"] * 1e3, 3),
+        "roofline": roofline_of(kv_b, flops, m["ms_part"], None),
+        "steps": m["steps"], "warmup": m["warmup"], "repeats": len(m["full"]),
+        "units": m["units"], "row_groups": m["row_groups"], "parts": m["parts"],
+        "data": "synthetic (pools drawn on the device)",
+    }
+
+
+def wk_kv_bytes(wl):
+    from mla_split_kv_decode_amd import workloads as wk
+
+    return wk.kv_bytes(wl.seq_lens, wl.kv_format)
+
+
+def wk_flops(wl):
+    from mla_split_kv_decode_amd import workloads as wk
+
+    return wk.attention_flops(wl.seq_lens, wl.q_len, wl.num_heads, wl.causal)
+
+
+def read_ceiling(args, mb, wk, wl, nl):
+    """A plain read of the workload's rotated pools: every byte once, into registers or
+    into LDS as the partial stage copies them, one launch per pool; and an empty launch.
+    The floor of any single launch per layer-step that streams the same bytes."""
+    import torch
+
+    st = setup(mb, wk, wl, 0, nl)
+    kv_b = wk.kv_bytes(wl.seq_lens, wl.kv_format)
+    # exactly the KV bytes of each pool (its first pages; the pool's spare pages are left out)
+    pools = [p.view(torch.uint8).view(-1)[:kv_b] for p, _ in st["pools"]]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool_b = kv_b
+    out = {}
+    for mode, name in ((0, "registers"), (1, "lds_copies"), (2, "empty_launch")):
+        res = time_steps(lambda i: mb.read_reference(pools[i], mode, sink), args.steps, args.warmup,
+                         args.repeats, nl)
+        us = float(np.median(res)) * 1e3
+        out[name] = {"us_per_launch": round(us, 3)}
+        if mode != 2:
+            out[name]["GBps"] = round(pool_b / (us * 1e-6) / 1e9, 2)
+            out[name]["pct_of_8TBs"] = round(100 * pool_b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)
+    print(json.dumps({
+        "metric": "plain read of the rotated KV pools (one launch per pool): µs and GB/s",
+        "value": out["lds_copies"]["GBps"], "unit": "GB/s", "higher_is_better": True, "n_gpus": 1,
+        "data": "synthetic", "config": {"workload": describe(wl, 0), "bytes_read_per_launch": pool_b,
+                                        "layers_rotated": nl},
+        "steps": args.steps, "warmup": args.warmup, "repeats": args.repeats,
+        "reads": out,
+        "target_us_at_70pct": round(kv_b / (0.7 * HBM_PEAK_GBS * 1e9) * 1e6, 3),
+    }), flush=True)
+
+
+def bench_append(args, wl, mb, st, nl):
     """µs per mla_kv_append of the step's B x T new latents into one layer's pool, alone
-    and followed by that layer's decode (graph replay over the rotated pools)."""
+    and followed by that layer's decode."""
     import torch
 
     B, T = wl.batch, wl.q_len
     rng = np.random.default_rng(5)
     lat = torch.from_numpy(rng.standard_normal((B, T, 576)).astype(np.float32)).to(torch.bfloat16).cuda()
-    stream = torch.cuda.current_stream()
-
-    def timed(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(nl):
-                fn(i)
-        reps = max(1, args.steps // nl)
-        for _ in range(max(1, args.warmup // nl)):
-            g.replay()
-        torch.cuda.synchronize()
-        res = []
-        for _ in range(args.repeats):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-            e1.synchronize()
-            res.append(e0.elapsed_time(e1) / (reps * nl) * 1e3)
-        return float(np.median(res))
+    pools, step, kv_dtype = st["pools"], st["step"], st["kv_dtype"]
 
     def append(i):
-        mb.kv_append(pools[i % nl], dev0["block_table"], dev0["seq_lens"], lat, kv_dtype, scales[i % nl])
+        mb.kv_append(pools[i][0], st["bt"], st["sl"], lat, kv_dtype, pools[i][1])
 
-    def append_then_decode(i):
+    def both(i):
         append(i)
-        decode_step(i)
+        step(i)
 
-    us_app = timed(append)
-    us_both = timed(append_then_decode)
-    us_dec = timed(lambda i: decode_step(i))
-    elem = wk_elem(wl.kv_format)
-    moved = B * T * 576 * (2 + elem)
+    med = lambda f: float(np.median(time_steps(f, args.steps, args.warmup, args.repeats, nl))) * 1e3
+    us_app, us_both, us_dec = med(append), med(both), med(lambda i: step(i))
+    moved = B * T * 576 * (2 + (2 if wl.kv_format == "bf16" else 1))
     print(json.dumps({
         "metric": "MLA cache append us per layer (the step's new latents, FP8 quantised or bf16)",
         "value": round(us_app, 3), "unit": "us", "higher_is_better": False, "n_gpus": 1,
@@ -172,20 +331,18 @@ def bench_append(args, wl, mb, pools, scales, dev0, kv_dtype, decode_step, nl):
         "config": {"workload": describe(wl, 0), "new_rows": B * T},
         "append_GBps": round(moved / (us_app * 1e-6) / 1e9, 3),
         "append_then_decode_us": round(us_both, 3), "decode_us": round(us_dec, 3),
-        "bytes_per_append": moved,
+        "bytes_per_append": moved, "steps": args.steps, "warmup": args.warmup,
     }))
-
-
-def wk_elem(kv_format):
-    return 2 if kv_format == "bf16" else 1
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
-              f"multi-GPU path: run with --gpus 1", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this library has no "
+              f"multi-GPU path; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.repeats < 1:
+        sys.exit("--steps and --repeats must be >= 1, --warmup >= 0")
     import torch
 
     from mla_split_kv_decode_amd import binding as mb
@@ -202,93 +359,30 @@ def main():
         if "seq_len" not in spec:
             sys.exit("--q-len needs a workload with one history length")
         over = dict(q_len=args.q_len, seq_len=spec["seq_len"] - spec["q_len"] + args.q_len)
-    wl = wk.make_workload(args.workload, **over)
-    splits = 0 if args.splits == "auto" else int(args.splits)
-    kv_dtype = mb.MLA_BF16 if wl.kv_format == "bf16" else mb.MLA_FP8_E4M3FN
     nl = max(1, args.layers)
-
+    big = args.workload in ("ragged", "spec_verify")
     t_gen = time.perf_counter()
-    dev0 = wk.to_device(wl)
-    pools, scales = [dev0["pool"]], [dev0["kv_scale"]]
-    for layer in range(1, nl):
-        pool, sc = wk.layer_pool(wl, layer)
-        t = torch.from_numpy(pool.view(np.int16) if wl.kv_format == "bf16" else pool).cuda()
-        pools.append(t.view(torch.bfloat16) if wl.kv_format == "bf16" else t)
-        scales.append(float(sc))
+    # the two gigabyte-sized workloads get their timing pools on the device; the others
+    # use the oracle's generator (also for the CPU baseline)
+    wl = wk.timing_workload(args.workload, **over) if big else wk.make_workload(args.workload, **over)
     t_gen = time.perf_counter() - t_gen
+    splits = 0 if args.splits == "auto" else int(args.splits)
 
-    t_plan = time.perf_counter()
-    plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
-                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype,
-                   partials_bf16=args.partial == "bf16", fp8_qk=args.fp8_qk)
-    t_plan = time.perf_counter() - t_plan
-    ws = mb.workspace(plan)
-    B, T, H = wl.batch, wl.q_len, wl.num_heads
-    out = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
-    kvs = [mb.paged_kv(p, dev0["block_table"], dev0["seq_lens"], kv_dtype, s)
-           for p, s in zip(pools, scales)]
-    q = dev0["q"]
-
-    def step(i, full=True):
-        mb.decode_splitkv(plan, q, kvs[i % nl], ws, out=out if full else None,
-                          out_dtype=mb.MLA_BF16, out_lse=lse if full else None)
-
+    if args.read_ceiling:
+        read_ceiling(args, mb, wk, wl, nl)
+        return
     if args.append:
-        bench_append(args, wl, mb, pools, scales, dev0, kv_dtype, step, nl)
+        st = setup(mb, wk, wl, splits, nl, args.fp8_qk, device_pools=big)
+        bench_append(args, wl, mb, st, nl)
         return
 
-    def timed(full, steps):
-        """Average ms per call over `steps` calls (events on the launch stream)."""
-        stream = torch.cuda.current_stream()
-        if args.mode == "graph":
-            # one graph of `nl` consecutive layer-steps, replayed
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(nl):
-                    step(i, full)
-            reps = max(1, steps // nl)
-            for _ in range(max(1, args.warmup // nl)):
-                g.replay()
-            torch.cuda.synchronize()
-            res = []
-            for _ in range(args.repeats):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(reps):
-                    g.replay()
-                e1.record(stream)
-                e1.synchronize()
-                res.append(e0.elapsed_time(e1) / (reps * nl))
-            return res, reps * nl
-        for i in range(args.warmup):
-            step(i, full)
-        torch.cuda.synchronize()
-        res = []
-        for _ in range(args.repeats):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(steps):
-                step(i, full)
-            e1.record(stream)
-            e1.synchronize()
-            res.append(e0.elapsed_time(e1) / steps)
-        return res, steps
-
-    step(0)  # first call outside any capture (sets kernel attributes)
-    torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    full_ms, n_full = timed(True, args.steps)
-    part_ms, _ = timed(False, args.steps)
-    ms = float(np.median(full_ms))
-    ms_part = float(np.median(part_ms))
-
+    m = measure(args, mb, wk, wl, splits, nl, args.fp8_qk, device_pools=big)
     kv_b = wk.kv_bytes(wl.seq_lens, wl.kv_format)
-    gbs = kv_b / (ms * 1e-3) / 1e9
-    part_gbs = kv_b / (ms_part * 1e-3) / 1e9
     flops = wk.attention_flops(wl.seq_lens, wl.q_len, wl.num_heads, wl.causal)
+    ms, ms_part = m["ms"], m["ms_part"]
+    gbs = kv_b / (ms * 1e-3) / 1e9
     traffic = None
-    tr = None if args.fp8_qk else TRAFFIC.get((wl.name, splits, args.partial, mb.version()))
+    tr = None if args.fp8_qk else TRAFFIC.get((wl.name, splits, mb.version()))
     if tr:
         traffic = int(1024 * (tr["fetch_kib"] * tr["fetch_factor"] + tr["write_kib"] * tr["write_factor"]))
     res = {
@@ -296,48 +390,54 @@ def main():
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": n_full,
-        "warmup": args.warmup,
+        "steps": m["steps"],
+        "warmup": m["warmup"],
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if wl.kv_format == "bf16" else "fp8_e4m3fn KV, bf16 q and MFMA",
         "data": "synthetic",
         "config": {
             "workload": describe(wl, splits),
-            "batch": B, "q_len": T, "num_heads": H, "seq_len": int(wl.seq_lens.max()),
-            "kv_dtype": wl.kv_format, "splits": "auto" if splits == 0 else splits,
-            "layers_rotated": nl, "launch": args.mode, "partials": args.partial,
+            "batch": wl.batch, "q_len": wl.q_len, "num_heads": wl.num_heads,
+            "seq_len": int(wl.seq_lens.max()), "kv_dtype": wl.kv_format,
+            "splits": "auto" if splits == 0 else splits, "layers_rotated": nl,
             "qk": "fp8" if args.fp8_qk else "bf16",
         },
         "us_per_layer_step": round(ms * 1e3, 3),
         "pct_of_8TBs": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(part_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "mla_partial_kernel",
-            "kernel_us": round(ms_part * 1e3, 3),
-            "bytes_per_launch": kv_b,
-        },
+        "roofline": roofline_of(kv_b, flops, ms_part, traffic),
         "detail": {
-            "full_ms_repeats": [round(x, 6) for x in full_ms],
-            "partial_ms_repeats": [round(x, 6) for x in part_ms],
+            "timing": f"{m['warmup']} warm-up layer-steps, then {args.repeats} repeats of one graph "
+                      f"replay of {m['steps']} layer-steps (one untimed replay first); median",
+            "repeats": args.repeats,
+            "full_ms_repeats": [round(x, 6) for x in m["full"]],
+            "partial_ms_repeats": [round(x, 6) for x in m["part"]],
             "merge_and_gap_us": round((ms - ms_part) * 1e3, 3),
-            "units": plan.num_units, "row_groups": plan.row_groups, "parts": plan.num_parts,
+            "units": m["units"], "row_groups": m["row_groups"], "parts": m["parts"],
             "mfma_tflops": round(flops / (ms_part * 1e-3) / 1e12, 3),
             "mfma_frac_bf16": round(flops / (ms_part * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
             "io_bytes": wk.io_bytes(wl.seq_lens, wl.q_len, wl.num_heads, wl.kv_format),
-            "plan_host_us": round(t_plan * 1e6, 1),
+            "plan_host_us": round(m["t_plan"] * 1e6, 1),
             "input_gen_s": round(t_gen, 2),
+            "library": mb.version(),
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_other_workloads and args.workload == "long32k" and not over:
+        lines = {}
+        for name in ("tiny", "ragged", "spec_verify", "dcp_fp8"):
+            other = wk.timing_workload(name)
+            nlo = 2 if name in ("ragged", "spec_verify") else nl
+            st_o = max(4 * nlo, 48) if name in ("ragged", "spec_verify") else args.steps
+            mo = measure(args, mb, wk, other, 0, nlo, device_pools=True, steps=st_o,
+                         warmup=min(args.warmup, st_o))
+            lines[name] = compact_line(other, 0, mo)
+            print(f"[bench] {name}: {lines[name]['us_per_layer_step']} us/layer-step", file=sys.stderr,
+                  flush=True)
+        res["detail"]["workloads"] = lines
+    if not args.no_cpu_baseline and wl.pool is not None:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 

@@ -117,13 +117,7 @@ typedef struct {
  *                 page-aligned contiguous pieces per request (16 is the policy the
  *                 pages describe for the AITER assembly path, 1 the one-workgroup-
  *                 per-request policy of the older path)
- *   partials_bf16 storage of the partial answers between the two stages: 0 = fp32
- *                 (exact to fp32), 1 = bf16 (rounded to nearest even; the merge still
- *                 computes in fp32; half the workspace traffic).  A partial answer is
- *                 normalised, |O_p| <= max |value|, so bf16 storage moves the merged O by
- *                 at most 2^-9 of the largest |O_p|: negligible on long histories, where
- *                 |O| is small, but a second rounding on top of a bf16 output when a
- *                 few positions dominate and |O| is near max |value|.
+ * The partial answers between the two stages are kept in fp32 in the workspace.
  */
 typedef struct {
   int32_t batch;
@@ -132,7 +126,6 @@ typedef struct {
   float softmax_scale;
   int32_t causal;
   int32_t num_splits;
-  int32_t partials_bf16; /* 0: fp32 partial answers, 1: bf16 */
 } mla_decode_shape;
 
 typedef struct mla_plan mla_plan; /* opaque, host memory */
@@ -175,19 +168,6 @@ int32_t mla_plan_row_groups(const mla_plan* plan);
  */
 mla_status mla_plan_set_fp8_qk(mla_plan* plan, int32_t enable);
 /*
- * Optional per-(request, token) visibility (Kimi K3 on MI355X, section 1 "Cache", DCP8
- * paragraph, and the multi-token verification it extends to): hidden = device int32
- * [batch][q_len], caller-owned, read by every later decode call with this plan (keep it
- * alive and unchanged meanwhile).  Token t of request r then attends to the first
- * seq_lens[r] - hidden[r][t] positions of its history (values below 0 count as 0; a
- * value of seq_lens[r] or more hides everything: that row's partial answer is empty,
- * LSE = -inf and O = 0).  This replaces the causal pattern (hidden = q_len - 1 - t), so
- * a decode-context-parallel shard whose local history ends with some of the draft tokens
- * can mask exactly the drafts each token may not see.  hidden = NULL restores the
- * shape's causal flag.  Errors: plan NULL (MLA_ERR_INVALID_ARGUMENT).
- */
-mla_status mla_plan_set_hidden(mla_plan* plan, const int32_t* hidden);
-/*
  * Host copy of the work list, for inspection: 5 int32 per piece
  * (workgroup, request, first page, end page (exclusive), partial slot), in workgroup
  * order.  Writes at most `capacity` pieces; returns the number of pieces, or -1 on a
@@ -207,17 +187,27 @@ int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity);
  *   out_lse    fp32 [batch][q_len][num_heads] natural-log LSE, or NULL.  With it the
  *              result is a DCP shard's partial answer (section 1): merge shards with
  *              mla_merge_lse.
+ *   hidden     NULL (the shape's causal flag decides what each token sees), or device
+ *              int32 [batch][q_len], 4-byte aligned, read during this call only: token t
+ *              of request r then attends to the first seq_lens[r] - hidden[r][t]
+ *              positions of its history (values below 0 count as 0; seq_lens[r] or more
+ *              hides everything, and that row's answer is empty: LSE = -inf, O = 0).
+ *              This replaces the causal pattern (causal is hidden = q_len - 1 - t), so a
+ *              decode-context-parallel shard whose local history ends with some of the
+ *              draft tokens masks exactly the drafts each token may not see (section 1
+ *              "Cache", DCP8 paragraph, and the multi-token verification it extends to).
  * The two stages run as two kernels back to back on `stream`.  With out == NULL and
  * out_lse == NULL only the partial stage runs and the partials stay in the workspace:
- * at byte 0, O of partial_dtype [rows][16][num_parts][32] (row = token * num_heads +
- * head; the 512 columns in 16 chunks of 32, each chunk's parts contiguous); then, at the
- * next 256-byte boundary, fp32 LSE [rows][num_parts].  The parts of request r are the
- * slots that mla_plan_get_work lists for it.
+ * at byte 0, fp32 O [rows][16][num_parts][32] (row = token * num_heads + head; the 512
+ * columns in 16 chunks of 32, each chunk's parts contiguous); then, at the next 256-byte
+ * boundary, fp32 LSE [rows][num_parts].  The parts of request r are the slots that
+ * mla_plan_get_work lists for it.
  * Calls that share a workspace must be ordered on one stream.
  */
 mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_paged_kv* kv,
                               void* workspace, size_t workspace_bytes, void* out,
-                              int32_t out_dtype, float* out_lse, void* stream);
+                              int32_t out_dtype, float* out_lse, const int32_t* hidden,
+                              void* stream);
 
 /*
  * Merge partial answers that carry their LSE (section 1, DCP8 paragraph; section 4,
@@ -266,6 +256,25 @@ mla_status mla_kv_append(void* pool, int64_t num_pages, int32_t page_size, int32
 mla_status mla_block_table_check(const int32_t* block_table_host, int32_t batch,
                                  int32_t max_pages_per_seq, const int32_t* seq_lens_host,
                                  int32_t page_size, int64_t num_pages);
+
+/*
+ * Bandwidth reference, for measurement only (the post's roofline is the 8 TB/s HBM figure
+ * of its MI355X specification table, and "What to optimise next" asks for measured
+ * limits): one kernel that reads every byte of [buf, buf + bytes) once and does nothing
+ * else, so its time is the floor any single launch that streams the same bytes can
+ * reach on this device.
+ *   mode 0  plain 128-bit vector loads into registers (4,096 workgroups, grid-stride)
+ *   mode 1  128-bit direct copies into LDS, 144 KiB per workgroup: the copy the partial
+ *           stage issues for its pages, without the attention arithmetic
+ *   mode 2  an empty kernel (one workgroup): the cost of a launch; buf, bytes and sink
+ *           are ignored
+ *   buf     device memory, 16-byte aligned; bytes a multiple of 1024
+ *   sink    device uint32, 4-byte aligned; written only if a checksum of the data hits
+ *           one fixed 96-bit pattern (so in practice never)
+ * Enqueued on `stream`.  Errors: MLA_ERR_INVALID_ARGUMENT for a bad mode, pointer,
+ * alignment or size; MLA_ERR_DEVICE if the launch fails.
+ */
+mla_status mla_read_reference(const void* buf, size_t bytes, int32_t mode, uint32_t* sink, void* stream);
 
 /* Bytes of one page: page_size * 576 * element size; 0 for an unsupported dtype. */
 size_t mla_page_bytes(int32_t page_size, int32_t kv_dtype);

@@ -16,10 +16,11 @@
 
 namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, bool fp8_qk, hipStream_t stream);
-bool partial_nt_parts(bool part_bf16, int64_t max_row_slots);
+bool partial_nt_parts(int64_t max_row_slots);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
                         int max_row_slots, hipStream_t stream);
 size_t partial_lds_size(bool fp8, int rbw);
+hipError_t launch_read_reference(const void* buf, int64_t bytes, int mode, uint32_t* sink, hipStream_t stream);
 hipError_t launch_kv_append(void* pool, int64_t num_pages, bool fp8, const int32_t* block_table,
                             int32_t max_pages, const int32_t* seq_lens, const void* latents,
                             int32_t rows, int32_t q_len, float kv_scale, hipStream_t stream);
@@ -41,9 +42,7 @@ struct mla_plan {
   int32_t num_wg;        // work units of the partial stage
   int32_t num_splits;    // S (SPLIT_FIXED)
   int32_t num_slots;     // partial answers the workspace holds
-  int32_t part_bf16;     // partial O element type
   int32_t fp8_qk;        // QK^T on the FP8 matrix cores (mla_plan_set_fp8_qk)
-  const int32_t* hidden; // per-(request, token) hidden tails, device (mla_plan_set_hidden)
   int64_t total_pages;
   int32_t max_req_pages;  // largest ceil(seq_len / page) of a request
   int32_t max_req_slots;  // most partial answers of one request
@@ -156,8 +155,6 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
   if (s.causal != 0 && s.causal != 1) return fail(MLA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   if (s.num_splits < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
-  if (s.partials_bf16 != 0 && s.partials_bf16 != 1)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "partials_bf16 must be 0 or 1");
   if (page_size != kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (only %d)", page_size, kPage);
   if (kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3FN)
     return fail(MLA_ERR_UNSUPPORTED, "kv_dtype %d", kv_dtype);
@@ -247,10 +244,9 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
     }
     pl->max_req_slots = (int32_t)most;
   }
-  pl->part_bf16 = s.partials_bf16;
-  // [partial O | fp32 partial LSE], each 256-byte aligned
+  // [fp32 partial O | fp32 partial LSE], each 256-byte aligned
   pl->o_offset = 0;
-  pl->o_bytes = align256((size_t)slots * pl->rows * kDV * (pl->part_bf16 ? 2 : 4));
+  pl->o_bytes = align256((size_t)slots * pl->rows * kDV * sizeof(float));
   pl->lse_offset = pl->o_offset + pl->o_bytes;
   pl->workspace_bytes = pl->lse_offset + align256((size_t)slots * pl->rows * sizeof(float));
   if (workspace_bytes) *workspace_bytes = pl->workspace_bytes;
@@ -265,12 +261,6 @@ int32_t mla_plan_num_units(const mla_plan* plan) { return plan ? plan->num_wg : 
 int32_t mla_plan_num_parts(const mla_plan* plan) { return plan ? plan->num_slots : -1; }
 
 int32_t mla_plan_row_groups(const mla_plan* plan) { return plan ? plan->row_groups : -1; }
-
-mla_status mla_plan_set_hidden(mla_plan* plan, const int32_t* hidden) {
-  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "null plan");
-  plan->hidden = hidden;
-  return ok();
-}
 
 mla_status mla_plan_set_fp8_qk(mla_plan* plan, int32_t enable) {
   if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "null plan");
@@ -319,7 +309,7 @@ int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity) 
 
 mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_paged_kv* kv,
                               void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
-                              float* out_lse, void* stream) {
+                              float* out_lse, const int32_t* hidden, void* stream) {
   if (!plan || !q || !kv || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   if (!kv->pool || !kv->block_table || !kv->seq_lens)
     return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer in the KV descriptor");
@@ -354,10 +344,11 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
     if (!aligned(out, 16)) return fail(MLA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
   }
   if (out_lse && !aligned(out_lse, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "out_lse misaligned");
+  if (hidden && !aligned(hidden, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "hidden misaligned");
 
   const mla_decode_shape& s = plan->shape;
   hipStream_t st = (hipStream_t)stream;
-  void* part_o = (char*)workspace + plan->o_offset;
+  float* part_o = (float*)((char*)workspace + plan->o_offset);
   float* part_lse = (float*)((char*)workspace + plan->lse_offset);
 
   PartialParams pp{};
@@ -381,14 +372,13 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   pp.num_wg = plan->num_wg;
   pp.num_splits = plan->num_splits;
   pp.num_slots = plan->num_slots;
-  pp.part_bf16 = plan->part_bf16;
   pp.total_pages = plan->total_pages;
   const float log2e = 1.44269504088896341f;
   pp.score_scale = s.softmax_scale * log2e * (fp8 ? kv->kv_scale : 1.0f);
   pp.v_scale = fp8 ? kv->kv_scale : 1.0f;
   fill_plan_args(*plan, &pp.plan);
-  pp.hidden = plan->hidden;
-  pp.nt_parts = partial_nt_parts(plan->part_bf16 != 0, plan->max_req_slots);
+  pp.hidden = hidden;
+  pp.nt_parts = partial_nt_parts(plan->max_req_slots);
   if (!out && !out_lse) {
     if (plan->num_wg > 0) {
       hipError_t e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);
@@ -418,7 +408,7 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
     e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);
     if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
   }
-  e = launch_merge(mp, plan->part_bf16, true, (int64_t)s.batch * plan->rows, plan->max_req_slots, st);
+  e = launch_merge(mp, false, true, (int64_t)s.batch * plan->rows, plan->max_req_slots, st);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -445,6 +435,19 @@ mla_status mla_kv_append(void* pool, int64_t num_pages, int32_t page_size, int32
   hipError_t e = launch_kv_append(pool, num_pages, fp8, block_table, max_pages_per_seq, seq_lens,
                                   latents, batch * q_len, q_len, kv_scale, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mla_status mla_read_reference(const void* buf, size_t bytes, int32_t mode, uint32_t* sink, void* stream) {
+  if (mode < 0 || mode > 2) return fail(MLA_ERR_INVALID_ARGUMENT, "mode must be 0, 1 or 2");
+  if (mode != 2) {
+    if (!buf || !sink) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    if (bytes % 1024 != 0 || bytes > ((size_t)1 << 40))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "bytes must be a multiple of 1024 (and below 1 TiB)");
+  }
+  hipError_t e = launch_read_reference(buf, (int64_t)bytes, mode, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "read reference launch: %s", hipGetErrorString(e));
   return ok();
 }
 

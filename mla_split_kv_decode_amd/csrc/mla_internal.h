@@ -45,7 +45,7 @@ constexpr int kMaxRowBlocks = 64;  // q_len * ceil(heads / 16) limit of one call
 enum SplitMode : int32_t { SPLIT_BALANCED = 0, SPLIT_FIXED = 1 };
 
 // Partial answers between the two stages, in the workspace (slots = the plan's parts):
-//   O   [rows][kDV / kMergeCols chunks][slots][kMergeCols] of the partial element type
+//   O   [rows][kDV / kMergeCols chunks][slots][kMergeCols] fp32
 //   LSE [rows][slots] fp32
 // rows = q_len * num_heads, token-major then head; request r's pieces use its own slot
 // range.  A merge unit (row, column chunk) of a request thus reads one contiguous block.
@@ -106,7 +106,7 @@ struct PartialParams {
   const uint8_t* pool;        // [num_pages][64][576] of the KV element type
   const int32_t* block_table; // [B][max_pages]
   const int32_t* seq_lens;    // [B]
-  void* part_o;               // partial O (layout above), bf16 or fp32
+  float* part_o;              // fp32 partial O (layout above)
   float* part_lse;            // fp32 [rows][slots]
   int64_t num_pages;
   int32_t max_pages;
@@ -118,7 +118,6 @@ struct PartialParams {
   int32_t num_wg;     // W work units
   int32_t num_splits; // S (SPLIT_FIXED)
   int32_t num_slots;  // slot stride of the partial layout
-  int32_t part_bf16;  // partial O element type: 1 bf16, 0 fp32
   int64_t total_pages; // P from the plan's host copy of seq_lens (SPLIT_BALANCED)
   float score_scale;  // softmax_scale * log2(e) * kv_scale: scores in log2 units
   float v_scale;      // kv_scale applied to the value rows (1 for bf16)

@@ -194,6 +194,63 @@ def layer_pool(wl, layer, seed=None):
     return pool, scale
 
 
+def timing_workload(name, seed=None, **overrides):
+    """A named workload's lengths, block table and queries drawn exactly as
+    ``make_workload`` draws them, with no pool (``pool`` is None): for timing runs whose
+    pools are drawn on the device (``device_pools``), where drawing a gigabyte-sized
+    pool on the host would take most of the run."""
+    spec = dict(CONFIGS[name]) if name is not None else {}
+    spec.update(overrides)
+    if seed is None:
+        seed = list(CONFIGS).index(name) + 1 if name in CONFIGS else 0
+    rng = np.random.default_rng(seed)
+    batch = int(spec["batch"])
+    if "seq_lens" in spec:
+        seq_lens = np.asarray(spec["seq_lens"], dtype=np.int32)
+    elif "seq_len_range" in spec:
+        lo, hi = spec["seq_len_range"]
+        seq_lens = rng.integers(lo, hi + 1, size=batch).astype(np.int32)
+    else:
+        seq_lens = np.full(batch, int(spec["seq_len"]), dtype=np.int32)
+    page_size = int(spec.get("page_size", PAGE_SIZE))
+    total_pages = int(sum(-(-int(L) // page_size) for L in seq_lens))
+    num_pages = total_pages + SPARE_PAGES
+    perm = rng.permutation(num_pages) if spec.get("shuffled", True) else np.arange(num_pages)
+    block_table, spare = build_block_table(seq_lens, page_size, perm)
+    q_len, num_heads = int(spec["q_len"]), int(spec["num_heads"])
+    q_bits = to_bf16_bits(rng.standard_normal((batch, q_len, num_heads, D_LATENT), dtype=np.float32))
+    return Workload(
+        name=name or "custom", seed=int(seed), batch=batch, q_len=q_len, num_heads=num_heads,
+        seq_lens=seq_lens, kv_format=spec.get("kv_format", "bf16"), kv_scale=np.float32(1.0),
+        block_table=block_table, pool=None, q_bits=q_bits,
+        softmax_scale=np.float32(spec.get("softmax_scale", SOFTMAX_SCALE)),
+        causal=bool(spec.get("causal", True)), num_splits=int(spec.get("num_splits", 0)),
+        page_size=page_size, extra={"spare_pages": spare, "num_pages": num_pages},
+    )
+
+
+def device_pools(wl, layers, seed, device="cuda"):
+    """`layers` pools of a timing workload drawn on the device with torch's seeded
+    generator: N(0,1) values rounded to bf16, or for FP8 divided by
+    sigma = max|x| / 448 and cast to E4M3FN (the same recipe as ``make_pool``, other
+    random numbers).  Returns a list of (pool tensor, kv_scale)."""
+    import torch
+
+    n = int(wl.extra["num_pages"])
+    g = torch.Generator(device=device)
+    out = []
+    for layer in range(layers):
+        g.manual_seed(int(seed) * 1000 + layer)
+        x = torch.randn((n, wl.page_size, D_LATENT), generator=g, device=device, dtype=torch.float32)
+        if wl.kv_format == "bf16":
+            out.append((x.to(torch.bfloat16), 1.0))
+        else:
+            sigma = float(np.float32(float(x.abs().max()) / E4M3FN_MAX))
+            out.append(((x / sigma).to(torch.float8_e4m3fn).view(torch.uint8), sigma))
+        del x
+    return out
+
+
 # ---------------------------------------------------------------- counters
 
 def elem_bytes(kv_format):

@@ -63,9 +63,9 @@ def test_block_table_check(lib):
 
 
 def plan_status(batch=1, q_len=1, heads=16, seq_lens=(1024,), scale=TAU, causal=1, splits=0,
-                page=64, dtype=mb.MLA_BF16, cus=256, partial=0):
+                page=64, dtype=mb.MLA_BF16, cus=256):
     lib = mb.load()
-    shape = mb.MlaDecodeShape(batch, q_len, heads, scale, causal, splits, partial)
+    shape = mb.MlaDecodeShape(batch, q_len, heads, scale, causal, splits)
     sl = np.asarray(seq_lens, dtype=np.int32)
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
@@ -100,9 +100,6 @@ def test_plan_argument_checks():
     assert plan_status(heads=1025) == U  # 65 row blocks
     assert plan_status(q_len=5, heads=208, seq_lens=(100,)) == U  # 65 row blocks
     assert plan_status(cus=-1) == E
-    assert plan_status(partial=1) == mb.MLA_OK
-    assert plan_status(partial=2) == E
-    assert plan_status(partial=-1) == E
 
 
 def _fake(addr=1 << 20):
@@ -129,21 +126,88 @@ def test_fp8_qk_option_rules(dtype, q_len, heads, want):
             mb.Plan(1, q_len, heads, [1000], TAU, kv_dtype=dtype, num_cus=256, fp8_qk=True)
 
 
-def test_hidden_tails_setter():
-    """mla_plan_set_hidden only records the caller's device pointer: any non-null plan
-    takes a pointer or NULL (which restores the causal pattern); a null plan is refused."""
-    lib = mb.load()
-    plan = mb.Plan(2, 4, 16, [1000, 700], TAU, num_cus=256)
-    assert lib.mla_plan_set_hidden(plan.handle, _fake(1 << 22)) == mb.MLA_OK
-    assert lib.mla_plan_set_hidden(plan.handle, None) == mb.MLA_OK
-    assert lib.mla_plan_set_hidden(None, None) == mb.MLA_ERR_INVALID_ARGUMENT
+def test_binding_refuses_bad_tensors(monkeypatch):
+    """The binding checks every tensor before the library sees it (the library takes any
+    address as a device pointer).  CPU tensors stand in for device tensors here (the GPU
+    check is patched out), so each refusal below is the shape / dtype / contiguity check
+    it names; nothing reaches the library."""
     import torch
 
-    with pytest.raises(ValueError):  # host memory is refused before the library sees it
-        plan.set_hidden(torch.zeros((2, 4), dtype=torch.int32))
-    with pytest.raises(ValueError):
-        plan.set_hidden(torch.zeros((4, 2), dtype=torch.int32))
-    plan.set_hidden(None)
+    with pytest.raises(ValueError, match="on a GPU"):
+        mb.paged_kv(torch.zeros(2, 64, 576, dtype=torch.bfloat16), torch.zeros(1, 2, dtype=torch.int32),
+                    torch.zeros(1, dtype=torch.int32), mb.MLA_BF16)
+    monkeypatch.setattr(mb, "_on_gpu", lambda x: True)
+    i32 = torch.int32
+    pool = torch.zeros(4, 64, 576, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 3, dtype=i32)
+    sl = torch.tensor([100, 5], dtype=i32)
+
+    def refused(fn, match):
+        with pytest.raises(ValueError, match=match):
+            fn()
+
+    refused(lambda: mb.paged_kv(np.zeros((4, 64, 576), np.uint16), bt, sl, mb.MLA_BF16), "torch")
+    refused(lambda: mb.paged_kv(pool.view(torch.uint8), bt, sl, mb.MLA_BF16), "dtype")
+    refused(lambda: mb.paged_kv(pool, bt, sl, mb.MLA_FP8_E4M3FN), "dtype")
+    mb.paged_kv(pool.view(torch.uint8).view(8, 64, 576), bt, sl, mb.MLA_FP8_E4M3FN, 0.5)  # valid
+    refused(lambda: mb.paged_kv(pool.view(2, 128, 576), bt, sl, mb.MLA_BF16), "pool must be")
+    refused(lambda: mb.paged_kv(pool.view(4, 64 * 576), bt, sl, mb.MLA_BF16), "pool must be")
+    refused(lambda: mb.paged_kv(pool, bt.to(torch.int64), sl, mb.MLA_BF16), "dtype")
+    refused(lambda: mb.paged_kv(pool, bt.t(), sl, mb.MLA_BF16), "shape|contiguous")
+    refused(lambda: mb.paged_kv(pool, bt, sl[:1], mb.MLA_BF16), "shape")
+    refused(lambda: mb.paged_kv(pool, bt, sl, 7), "kv_dtype")
+    kv = mb.paged_kv(pool, bt, sl, mb.MLA_BF16)
+    plan = mb.Plan(2, 1, 12, [100, 5], TAU, num_cus=256)
+    q = torch.zeros(2, 1, 12, 576, dtype=torch.bfloat16)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8)
+    out = torch.zeros(2, 1, 12, 512, dtype=torch.bfloat16)
+    lse = torch.zeros(2, 1, 12, dtype=torch.float32)
+
+    def dec(**kw):
+        args = dict(q=q, kv=kv, ws=ws, out=out, out_lse=lse)
+        args.update(kw)
+        return lambda: mb.decode_splitkv(plan, args["q"], args["kv"], args["ws"], out=args["out"],
+                                         out_lse=args["out_lse"], hidden=args.get("hidden"),
+                                         out_dtype=args.get("out_dtype", mb.MLA_BF16))
+
+    refused(dec(q=np.zeros((2, 1, 12, 576), np.uint16)), "torch")
+    refused(dec(q=q.float()), "dtype")
+    refused(dec(q=torch.zeros(2, 1, 16, 576, dtype=torch.bfloat16)), "shape")
+    refused(dec(q=torch.zeros(2, 1, 12, 1152, dtype=torch.bfloat16)[..., :576]), "contiguous")
+    refused(dec(ws=ws[:-1]), "workspace")
+    refused(dec(out=out.float()), "dtype")
+    refused(dec(out=out, out_dtype=mb.MLA_FP32), "dtype")
+    refused(dec(out=torch.zeros(2, 1, 12, 576, dtype=torch.bfloat16)), "shape")
+    refused(dec(out_lse=lse.double()), "dtype")
+    refused(dec(out_lse=torch.zeros(2, 12, dtype=torch.float32)), "shape")
+    refused(dec(hidden=torch.zeros(2, 1, dtype=torch.int64)), "dtype")
+    refused(dec(hidden=torch.zeros(1, 2, dtype=i32)), "shape")
+    refused(dec(kv=mb.paged_kv(pool, bt[:1], sl[:1], mb.MLA_BF16)), "requests")
+    refused(dec(kv=mb.MlaPagedKV()), "paged_kv")
+    lat = torch.zeros(2, 1, 576, dtype=torch.bfloat16)
+    refused(lambda: mb.kv_append(pool, bt, sl, lat.float(), mb.MLA_BF16), "dtype")
+    refused(lambda: mb.kv_append(pool, bt, sl, torch.zeros(3, 1, 576, dtype=torch.bfloat16), mb.MLA_BF16),
+            "latents")
+    refused(lambda: mb.kv_append(pool[:, :32].contiguous(), bt, sl, lat, mb.MLA_BF16), "pool must be")
+    po = torch.zeros(3, 4, 512, dtype=torch.float32)
+    pl = torch.zeros(3, 4, dtype=torch.float32)
+    refused(lambda: mb.merge_lse(po.double(), pl), "dtype")
+    refused(lambda: mb.merge_lse(po[..., :256], pl), "contiguous|part_o")
+    refused(lambda: mb.merge_lse(po, pl[:, :3]), "part_lse")
+    refused(lambda: mb.merge_lse(po, pl, out=torch.zeros(3, 512)), "out must")
+    refused(lambda: mb.merge_lse(po, pl, out_lse=torch.zeros(5)), "out_lse")
+
+
+def test_decode_refuses_misaligned_hidden():
+    """hidden is a per-call device argument; its alignment is checked on the host."""
+    lib = mb.load()
+    plan = mb.Plan(2, 4, 16, [1000, 700], TAU, num_cus=256)
+    kv = mb.MlaPagedKV(1 << 22, 32, 64, mb.MLA_BF16, 1.0, 1 << 21, 16, 1 << 23)
+    st = lib.mla_decode_splitkv(plan.handle, _fake(), ctypes.byref(kv), _fake(1 << 24),
+                                plan.workspace_bytes, _fake(1 << 25), mb.MLA_BF16, None,
+                                _fake((1 << 26) + 2), None)
+    assert st == mb.MLA_ERR_INVALID_ARGUMENT
+    assert "hidden" in lib.mla_last_error().decode()
 
 
 def test_kv_append_argument_checks_enqueue_nothing():
@@ -185,7 +249,7 @@ def test_decode_argument_checks_enqueue_nothing():
     def call(q=_fake(), kvd=kv, wsp=_fake(1 << 24), wsb=ws, out=_fake(1 << 25), od=mb.MLA_BF16,
              lse=None):
         return lib.mla_decode_splitkv(plan.handle, q, ctypes.byref(kvd), wsp, wsb, out, od, lse,
-                                      None)
+                                      None, None)
 
     E = mb.MLA_ERR_INVALID_ARGUMENT
     assert call(q=None) == E
@@ -209,7 +273,7 @@ def test_decode_argument_checks_enqueue_nothing():
         bad = mb.MlaPagedKV(1 << 22, 16, 64, mb.MLA_FP8_E4M3FN, s, 1 << 21, 16, 1 << 23)
         assert lib.mla_decode_splitkv(fplan.handle, _fake(), ctypes.byref(bad), _fake(1 << 24),
                                       fplan.workspace_bytes, _fake(1 << 25), mb.MLA_BF16, None,
-                                      None) == E
+                                      None, None) == E
     # merge checks
     assert lib.mla_merge_lse(None, mb.MLA_FP32, _fake(), 2, 4, _fake(), mb.MLA_BF16, None, None) == E
     assert lib.mla_merge_lse(_fake(), mb.MLA_FP32, _fake(), 0, 4, _fake(), mb.MLA_BF16, None, None) == E
@@ -313,9 +377,8 @@ def test_planner_row_groups(q_len, heads, cus):
     check_plan(seq_lens, q_len=q_len, heads=heads, splits=5, cus=cus)
 
 
-@pytest.mark.parametrize("partials_bf16,elem", [(True, 2), (False, 4)])
-def test_workspace_size(partials_bf16, elem):
-    plan = mb.Plan(2, 4, 16, [500, 1000], TAU, num_cus=256, partials_bf16=partials_bf16)
+def test_workspace_size():
+    plan = mb.Plan(2, 4, 16, [500, 1000], TAU, num_cus=256)
     rows = 4 * 16
-    o_bytes = -(-plan.num_parts * rows * 512 * elem // 256) * 256
+    o_bytes = -(-plan.num_parts * rows * 512 * 4 // 256) * 256
     assert plan.workspace_bytes == o_bytes + -(-plan.num_parts * rows * 4 // 256) * 256

@@ -3,8 +3,8 @@
 Gates (element by element, real heads only): max |O_gpu - O_oracle| <= 1e-2 with
 bf16 KV and <= 3e-2 with FP8 KV, max |LSE_gpu - LSE_oracle| <= 1e-3.  Exact
 (bitwise) equalities where the method fixes them: repeated runs, page
-permutation, padded heads.  Full-size workloads are checked on sampled
-requests / heads that the oracle computes one by one.
+permutation, padded heads.  The full-size workloads are compared on every request,
+token and real head.
 """
 
 import numpy as np
@@ -34,7 +34,7 @@ def kv_dtype_of(wl):
 
 
 def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, heads=None,
-            block_table=None, pool=None, canary=False, partial="fp32", fp8_qk=False, hidden=None):
+            block_table=None, pool=None, canary=False, fp8_qk=False, hidden=None):
     """Decode a workload on the GPU; returns (O fp64 [B][T][H][512], LSE fp64 [B][T][H])."""
     import torch
 
@@ -43,10 +43,10 @@ def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, head
         dev = dict(dev, block_table=torch.from_numpy(np.ascontiguousarray(block_table)).cuda())
     splits = wl.num_splits if num_splits is None else num_splits
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale,
-                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype_of(wl),
-                   partials_bf16=partial == "bf16", fp8_qk=fp8_qk)
+                   causal=wl.causal, num_splits=splits, kv_dtype=kv_dtype_of(wl), fp8_qk=fp8_qk)
+    hid = None
     if hidden is not None:
-        plan.set_hidden(torch.from_numpy(np.ascontiguousarray(hidden, dtype=np.int32)).cuda())
+        hid = torch.from_numpy(np.ascontiguousarray(hidden, dtype=np.int32)).cuda()
     ws = mb.workspace(plan)
     B, T, H = wl.batch, wl.q_len, wl.num_heads
     tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
@@ -58,7 +58,8 @@ def run_gpu(wl, num_splits=None, dev=None, out_dtype="bf16", want_lse=True, head
     kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], kv_dtype_of(wl),
                      dev["kv_scale"])
     mb.decode_splitkv(plan, dev["q"], kv, ws, out=out,
-                      out_dtype=mb.MLA_BF16 if out_dtype == "bf16" else mb.MLA_FP32, out_lse=lse)
+                      out_dtype=mb.MLA_BF16 if out_dtype == "bf16" else mb.MLA_FP32, out_lse=lse,
+                      hidden=hid)
     torch.cuda.synchronize()
     if canary:
         assert torch.all(out_buf[:pad] == 7.0) and torch.all(out_buf[-pad:] == 7.0)
@@ -140,13 +141,10 @@ def test_small_shapes(case):
 
 def test_fp32_output_and_no_lse():
     wl = wk.make_workload(None, seed=102, batch=2, q_len=1, num_heads=16, seq_lens=[333, 900])
-    o, l = run_gpu(wl, out_dtype="fp32", partial="fp32")
+    o, l = run_gpu(wl, out_dtype="fp32")
     o_ref, l_ref = run_oracle(wl)
-    eo, _ = compare(wl, o, l, o_ref, l_ref, "fp32 out, fp32 partials")
+    eo, _ = compare(wl, o, l, o_ref, l_ref, "fp32 out")
     assert eo <= 2e-3  # no bf16 rounding anywhere but P
-    o, l = run_gpu(wl, out_dtype="fp32", partial="bf16")
-    eo_b, _ = compare(wl, o, l, o_ref, l_ref, "fp32 out, bf16 partials")
-    assert eo_b <= 2e-3 + 2.0 ** -9 * 4.0  # one bf16 rounding of a part, |O_p| < 4
     o2, _ = run_gpu(wl, want_lse=False)
     assert np.abs(o2 - o_ref).max() <= TOL_O["bf16"]
 
@@ -170,19 +168,9 @@ def long32k():
     return wk.make_workload("long32k")
 
 
-@pytest.mark.parametrize("partial", ["bf16", "fp32"])
 @pytest.mark.parametrize("splits", [16, 0, 1])
-def test_long32k(long32k, splits, partial):
-    check_full(long32k, num_splits=splits, partial=partial)
-
-
-def test_partial_precision_gap(long32k):
-    """On a long history bf16 partial storage moves the bf16 output by about one output
-    rounding step, and never the LSE."""
-    o16, l16 = run_gpu(long32k, num_splits=0, partial="bf16")
-    o32, l32 = run_gpu(long32k, num_splits=0, partial="fp32")
-    assert np.abs(l16 - l32).max() <= 1e-6  # LSE never goes through bf16 (summation order only)
-    assert np.abs(o16 - o32).max() <= 2e-3
+def test_long32k(long32k, splits):
+    check_full(long32k, num_splits=splits)
 
 
 def test_long32k_seeds():
@@ -190,23 +178,31 @@ def test_long32k_seeds():
         check_full(wk.make_workload("long32k", seed=seed), num_splits=0)
 
 
-@pytest.mark.parametrize("partial", ["fp32", "bf16"])
-def test_ragged_sampled(partial):
+@pytest.fixture(scope="module")
+def ragged():
     wl = wk.make_workload("ragged")
-    o, l = run_gpu(wl, num_splits=0, partial=partial)
-    req = [0, 1, 17, 40, 63]
-    o_ref, l_ref = run_oracle(wl, requests=req)
-    compare(wl, o[req], l[req], o_ref, l_ref, "auto, sampled requests")
+    return wl, run_oracle(wl)
 
 
-@pytest.mark.parametrize("partial", ["fp32", "bf16"])
-def test_dcp_fp8_shard_sampled(partial):
+def test_ragged_full(ragged):
+    """All 64 requests (1,002,597 positions), every head, at auto splits."""
+    wl, (o_ref, l_ref) = ragged
+    o, l = run_gpu(wl, num_splits=0)
+    compare(wl, o, l, o_ref, l_ref, "auto, all 64 requests")
+
+
+@pytest.fixture(scope="module")
+def dcp_fp8():
     wl = wk.make_workload("dcp_fp8")
-    o, l = run_gpu(wl, partial=partial)
-    heads = [0, 11, 12, 47, 95]
-    req = [0, 3, 7]
-    o_ref, l_ref = run_oracle(wl, requests=req, heads=heads)
-    compare(wl, o[req][:, :, heads], l[req][:, :, heads], o_ref, l_ref, "shard, sampled")
+    return wl, run_oracle(wl)
+
+
+def test_dcp_fp8_shard_full(dcp_fp8):
+    """All 8 requests and all 96 heads (six row blocks, three row groups of two) of the
+    17,750-position FP8 shard."""
+    wl, (o_ref, l_ref) = dcp_fp8
+    o, l = run_gpu(wl)
+    compare(wl, o, l, o_ref, l_ref, "shard, every request and head")
 
 
 # ------------------------------------------------------------ FP8 matrix-core q.k (opt-in)
@@ -228,13 +224,10 @@ def test_fp8_qk_small_shapes(case):
     check_full(wl, canary=True, fp8_qk=True)
 
 
-def test_fp8_qk_dcp_shard_sampled():
-    wl = wk.make_workload("dcp_fp8")
+def test_fp8_qk_dcp_shard_full(dcp_fp8):
+    wl, (o_ref, l_ref) = dcp_fp8
     o, l = run_gpu(wl, fp8_qk=True)
-    heads = [0, 11, 12, 47, 95]
-    req = [0, 3, 7]
-    o_ref, l_ref = run_oracle(wl, requests=req, heads=heads)
-    compare(wl, o[req][:, :, heads], l[req][:, :, heads], o_ref, l_ref, "shard, FP8 q.k, sampled")
+    compare(wl, o, l, o_ref, l_ref, "shard, FP8 q.k, every request and head")
 
 
 def test_fp8_qk_agrees_with_bf16_qk():
@@ -281,8 +274,8 @@ def test_query_dynamic_range(fp8_qk):
 def _random_cases(n, seed=11):
     """Shapes drawn from a seeded generator: head counts with and without padding, one
     to four query tokens (causal or not), lengths from one page's worth to a few dozen
-    pages, every split policy, both pool formats, the FP8 q.k option on FP8 multi-row
-    shapes and, now and then, bf16 partial answers."""
+    pages, every split policy, both pool formats and the FP8 q.k option on FP8 multi-row
+    shapes."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -296,45 +289,31 @@ def _random_cases(n, seed=11):
         splits = int(rng.choice([0, 0, 1, 3, 16]))
         causal = bool(rng.integers(2))
         f8qk = kv == "fp8_e4m3fn" and T * -(-H // 16) >= 2 and bool(rng.integers(2))
-        partial = ["fp32", "bf16"][rng.integers(2)] if rng.integers(4) == 0 else "fp32"
-        cases.append((i, B, T, H, seq, splits, kv, causal, f8qk, partial))
+        if rng.integers(4) == 0:
+            rng.integers(2)  # (a draw kept so that the seeded shapes stay the same)
+        cases.append((i, B, T, H, seq, splits, kv, causal, f8qk))
     return cases
 
 
 @pytest.mark.parametrize("case", _random_cases(16), ids=lambda c: f"r{c[0]}")
 def test_random_shapes(case):
-    i, B, T, H, seq, splits, kv, causal, f8qk, partial = case
+    i, B, T, H, seq, splits, kv, causal, f8qk = case
     wl = wk.make_workload(None, seed=1000 + i, batch=B, q_len=T, num_heads=H, seq_lens=seq,
                           kv_format=kv, shuffled=True, num_splits=splits, causal=causal)
-    o, l = run_gpu(wl, canary=True, fp8_qk=f8qk, partial=partial)
+    o, l = run_gpu(wl, canary=True, fp8_qk=f8qk)
     o_ref, l_ref = run_oracle(wl)
-    what = f"B{B} T{T} H{H} s{splits} causal={causal} fp8qk={f8qk} partial={partial}"
-    if partial == "bf16":
-        # bf16 partial answers: a second rounding of up to 2^-9 of the largest |O_p|
-        # (the option's documented cost), checked against that bound on top of the bar
-        eo = float(np.abs(o - o_ref).max())
-        vmax = 0.0  # largest |value| any request attends to
-        for r, L in enumerate(wl.seq_lens):
-            rows = oracle.gather_latents(wl.pool, wl.block_table[r], int(L), wl.page_size)[:, :512]
-            vals = (oracle.bf16_bits_to_f64(rows) if kv == "bf16"
-                    else oracle.e4m3fn_codes_to_f64(rows) * float(wl.kv_scale))
-            vmax = max(vmax, float(np.abs(vals).max()))
-        print(f"[parity] random {what}: max|dO|={eo:.3e} (bar {TOL_O[kv] + vmax / 512:.3e})", flush=True)
-        assert eo <= TOL_O[kv] + vmax / 512, (what, eo)
-        assert float(np.abs(l - l_ref).max()) <= TOL_LSE
-    else:
-        compare(wl, o, l, o_ref, l_ref, what)
+    compare(wl, o, l, o_ref, l_ref, f"B{B} T{T} H{H} s{splits} causal={causal} fp8qk={f8qk}")
 
 
-@pytest.mark.parametrize("partial", ["fp32", "bf16"])
-def test_spec_verify_sampled(partial):
+def test_spec_verify_full():
+    """All 8 requests, 4 causal draft tokens each, 16 heads, 131,076 positions, at the
+    16 partitions of the pages' policy and at auto splits."""
     wl = wk.make_workload("spec_verify")
-    o16, l16 = run_gpu(wl, num_splits=16, partial=partial)
-    o0, l0 = run_gpu(wl, num_splits=0, partial=partial)
-    req = [0, 5]
-    o_ref, l_ref = run_oracle(wl, requests=req)
-    compare(wl, o16[req], l16[req], o_ref, l_ref, "16 splits, sampled")
-    compare(wl, o0[req], l0[req], o_ref, l_ref, "auto, sampled")
+    o_ref, l_ref = run_oracle(wl)
+    o16, l16 = run_gpu(wl, num_splits=16)
+    compare(wl, o16, l16, o_ref, l_ref, "16 splits, all requests")
+    o0, l0 = run_gpu(wl, num_splits=0)
+    compare(wl, o0, l0, o_ref, l_ref, "auto, all requests")
 
 
 # ------------------------------------------------------------ DCP shards
@@ -739,9 +718,8 @@ def test_out_of_range_page_inside_the_page_loop(kv, T, H):
 
 # ------------------------------------------------------------ workspace layout
 
-@pytest.mark.parametrize("partial", ["bf16", "fp32"])
-def test_partial_only_layout(partial):
-    """With no outputs only the partial stage runs; the workspace then holds O as
+def test_partial_only_layout():
+    """With no outputs only the partial stage runs; the workspace then holds fp32 O as
     [rows][16][parts][32] and LSE as [rows][parts], and merging each request's parts
     (its slots from the work list) with the oracle's merge gives the oracle's answer."""
     import torch
@@ -749,16 +727,14 @@ def test_partial_only_layout(partial):
     wl = wk.make_workload(None, seed=610, batch=3, q_len=2, num_heads=12, seq_lens=[900, 70, 2500])
     dev = wk.to_device(wl)
     plan = mb.Plan(wl.batch, wl.q_len, wl.num_heads, wl.seq_lens, wl.softmax_scale, num_splits=0,
-                   partials_bf16=partial == "bf16", num_cus=24)
+                   num_cus=24)
     ws = mb.workspace(plan)
     kv = mb.paged_kv(dev["pool"], dev["block_table"], dev["seq_lens"], mb.MLA_BF16)
     mb.decode_splitkv(plan, dev["q"], kv, ws, out=None, out_lse=None)
     torch.cuda.synchronize()
     S, rows = plan.num_parts, wl.q_len * wl.num_heads
-    elem = 2 if partial == "bf16" else 4
-    o_bytes = -(-S * rows * 512 * elem // 256) * 256
-    raw = ws[:S * rows * 512 * elem]
-    o = (raw.view(torch.bfloat16) if partial == "bf16" else raw.view(torch.float32)).float()
+    o_bytes = -(-S * rows * 512 * 4 // 256) * 256
+    o = ws[:S * rows * 512 * 4].view(torch.float32)
     o = o.view(rows, 16, S, 32).permute(2, 0, 1, 3).reshape(S, rows, 512).cpu().numpy()
     lse = ws[o_bytes:o_bytes + S * rows * 4].view(torch.float32).view(rows, S).T.cpu().numpy()
     work = plan.work()
