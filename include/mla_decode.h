@@ -28,8 +28,9 @@
  *
  * Memory.  The caller owns every buffer.  Device buffers are plain device pointers
  * (hipMalloc / torch CUDA tensors).  The library allocates no device memory and never
- * keeps a pointer past a call.  A plan is host memory owned by the library
- * (mla_plan_create / mla_plan_destroy).
+ * keeps a pointer past a call (the scratch of mla_decode_splitkv_noalloc is a static
+ * device array of the library's code object, not an allocation).  A plan is host memory
+ * owned by the library (mla_plan_create / mla_plan_destroy).
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  * device work is enqueued on it; no call synchronises the host with the device.
@@ -208,6 +209,25 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
                               void* workspace, size_t workspace_bytes, void* out,
                               int32_t out_dtype, float* out_lse, const int32_t* hidden,
                               void* stream);
+
+/*
+ * Split-KV decode that allocates nothing, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mla_decode_splitkv with the partial answers kept in a scratch array the library holds,
+ * one per GPU (MLA_NOALLOC_SCRATCH_BYTES each, kept until the process ends), instead of
+ * a caller's workspace.  Arguments and results are those of mla_decode_splitkv, except
+ * that out and out_lse may not both be NULL (MLA_ERR_INVALID_ARGUMENT).  A plan whose
+ * workspace_bytes exceed MLA_NOALLOC_SCRATCH_BYTES is refused (MLA_ERR_UNSUPPORTED,
+ * nothing enqueued).  Every call on one GPU uses that GPU's one scratch array, which
+ * keeps the last call's partial answers (nothing in it needs to start cleared): calls
+ * ordered on one stream are fine, calls that overlap on one GPU (several streams, or
+ * host threads without ordering) race and must not be made.  The first call on a device
+ * looks up the array's address there (hipGetSymbolAddress; no allocation).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+mla_status mla_decode_splitkv_noalloc(const mla_plan* plan, const void* q, const mla_paged_kv* kv,
+                                      void* out, int32_t out_dtype, float* out_lse,
+                                      const int32_t* hidden, void* stream);
 
 /*
  * Merge partial answers that carry their LSE (section 1, DCP8 paragraph; section 4,

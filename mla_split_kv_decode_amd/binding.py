@@ -69,6 +69,7 @@ def _signatures():
         "mla_plan_get_work": (c.c_int32, [P, P, c.c_int32]),
         "mla_decode_splitkv": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_size_t, P, c.c_int32,
                                          P, P, P]),
+        "mla_decode_splitkv_noalloc": (c.c_int, [P, P, c.POINTER(MlaPagedKV), P, c.c_int32, P, P, P]),
         "mla_merge_lse": (c.c_int, [P, c.c_int32, P, c.c_int32, c.c_int64, P, c.c_int32, P, P]),
         "mla_kv_append": (c.c_int, [P, c.c_int64, c.c_int32, c.c_int32, c.c_float, P, c.c_int32, P, P,
                                     c.c_int32, c.c_int32, P]),
@@ -304,6 +305,29 @@ def decode_splitkv(plan, q, kv, ws, out=None, out_dtype=MLA_BF16, out_lse=None, 
     hp = _opt_device_tensor(hidden, "hidden", (torch.int32,), (B, T), dev)
     _check(load().mla_decode_splitkv(plan.handle, qp, ctypes.byref(kv), wsp, ws_bytes, op,
                                      int(out_dtype), lp, hp, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_splitkv_noalloc(plan, q, kv, out=None, out_dtype=MLA_BF16, out_lse=None, hidden=None,
+                           stream=None):
+    """mla_decode_splitkv_noalloc: decode_splitkv with the library's per-GPU scratch in
+    place of a workspace (nothing is allocated); same tensors and checks."""
+    import torch
+
+    if not isinstance(kv, MlaPagedKV) or not hasattr(kv, "device"):
+        raise ValueError("kv must come from paged_kv()")
+    dev = kv.device
+    B, T, H = plan.batch, plan.q_len, plan.num_heads
+    if kv.batch != B:
+        raise ValueError(f"the KV descriptor has {kv.batch} requests, the plan {B}")
+    qp = _device_tensor(q, "q", (torch.bfloat16,), (B, T, H, D_LATENT), dev)
+    op = _opt_device_tensor(out, "out", _out_dtypes(out_dtype), (B, T, H, D_V), dev)
+    lp = _opt_device_tensor(out_lse, "out_lse", (torch.float32,), (B, T, H), dev)
+    hp = _opt_device_tensor(hidden, "hidden", (torch.int32,), (B, T), dev)
+    _check(load().mla_decode_splitkv_noalloc(plan.handle, qp, ctypes.byref(kv), op, int(out_dtype),
+                                             lp, hp, _stream(stream)))
 
 
 def kv_append(pool, block_table, seq_lens, latents, kv_dtype, kv_scale=1.0, stream=None,

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -94,6 +95,45 @@ int wg_per_cu(bool fp8, int rbw) {
   const size_t cu_lds = 160 * 1024;
   int n = (int)(cu_lds / ((lds + 1279) / 1280 * 1280));
   return n < 1 ? 1 : (n > 2 ? 2 : n);
+}
+
+mla_status decode_impl(const mla_plan* plan, const void* q, const mla_paged_kv* kv, void* workspace,
+                       size_t workspace_bytes, void* out, int32_t out_dtype, float* out_lse,
+                       const int32_t* hidden, void* stream);
+
+// Scratch of the entry point that allocates nothing (mla_decode_splitkv_noalloc): the
+// partial answers between the two stages live in a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never takes the array's name as an
+// address (on the host it only stands for the symbol): each device's address comes from
+// hipGetSymbolAddress, looked up once per device on the first call made with that device
+// current, and that address is what the kernels receive.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on device d, null until looked up
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+mla_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d (at most %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLA_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    if (!aligned(p, 256)) return fail(MLA_ERR_DEVICE, "scratch on device %d is not 256-byte aligned", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
 }
 
 }  // namespace
@@ -310,6 +350,31 @@ int32_t mla_plan_get_work(const mla_plan* plan, int32_t* out, int32_t capacity) 
 mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_paged_kv* kv,
                               void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
                               float* out_lse, const int32_t* hidden, void* stream) {
+  return decode_impl(plan, q, kv, workspace, workspace_bytes, out, out_dtype, out_lse, hidden, stream);
+}
+
+mla_status mla_decode_splitkv_noalloc(const mla_plan* plan, const void* q, const mla_paged_kv* kv,
+                                      void* out, int32_t out_dtype, float* out_lse, const int32_t* hidden,
+                                      void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!out && !out_lse)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "out and out_lse are both NULL: the scratch is not the caller's to read");
+  if (plan->workspace_bytes > kScratchBytes)
+    return fail(MLA_ERR_UNSUPPORTED, "the plan needs %zu bytes of partial answers; the no-allocation scratch holds %zu",
+                plan->workspace_bytes, kScratchBytes);
+  void* ws = nullptr;
+  const mla_status st = scratch_of_current_device(&ws);
+  if (st != MLA_OK) return st;
+  return decode_impl(plan, q, kv, ws, kScratchBytes, out, out_dtype, out_lse, hidden, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+mla_status decode_impl(const mla_plan* plan, const void* q, const mla_paged_kv* kv, void* workspace,
+                       size_t workspace_bytes, void* out, int32_t out_dtype, float* out_lse,
+                       const int32_t* hidden, void* stream) {
   if (!plan || !q || !kv || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   if (!kv->pool || !kv->block_table || !kv->seq_lens)
     return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer in the KV descriptor");
@@ -412,6 +477,10 @@ mla_status mla_decode_splitkv(const mla_plan* plan, const void* q, const mla_pag
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 mla_status mla_kv_append(void* pool, int64_t num_pages, int32_t page_size, int32_t kv_dtype,
                          float kv_scale, const int32_t* block_table, int32_t max_pages_per_seq,
