@@ -13,8 +13,9 @@ memory-side cache.  Inputs are synthetic and already resident in HBM.
 
 Timing: W untimed warm-up layer-steps, then R repeats of exactly K layer-steps, each
 repeat one replay of a graph holding the K steps, bracketed by HIP events on the launch
-stream; a device-side sleep queued before the first event keeps the host's launch of
-the replay out of the timed region.  The reported time is the median repeat / K.
+stream and queued right behind an untimed replay of the same graph (so the GPU is busy
+and at its working clocks when the timed region starts, and the host's launch of the
+replay is not in it).  The reported time is the median repeat / K.
 
 The JSON line reports KV-read GB/s (algorithmic KV bytes / time per layer-step, each
 cached latent read once) and the time per layer-step.  `roofline` prices the partial
@@ -103,8 +104,11 @@ def describe(wl, splits):
 
 
 def time_steps(step, steps, warmup, repeats, nl):
-    """Median ms per layer-step over `repeats` replays of a graph of exactly `steps`
-    layer-steps (layer i % nl), after `warmup` eager layer-steps and one untimed replay."""
+    """Per-repeat ms per layer-step: `warmup` eager layer-steps, then `repeats` times an
+    untimed replay of a graph of exactly `steps` layer-steps (layer i % nl) followed by a
+    timed replay of the same graph.  The timed replay is queued behind the untimed one, so
+    the GPU is busy (and at its working clocks) when the timed region starts, and the
+    host's launch of the replay is not in it."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -114,14 +118,13 @@ def time_steps(step, steps, warmup, repeats, nl):
     with torch.cuda.graph(g):
         for i in range(steps):
             step(i % nl)
-    g.replay()
     torch.cuda.synchronize()
     res = []
     for _ in range(repeats):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(8_000_000)  # the GPU is busy while the replay is queued behind e0
+        g.replay()  # untimed
         e0.record(stream)
-        g.replay()
+        g.replay()  # timed: exactly `steps` layer-steps
         e1.record(stream)
         e1.synchronize()
         res.append(e0.elapsed_time(e1) / steps)
@@ -409,8 +412,9 @@ def main():
         "pct_of_8TBs": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": roofline_of(kv_b, flops, ms_part, traffic),
         "detail": {
-            "timing": f"{m['warmup']} warm-up layer-steps, then {args.repeats} repeats of one graph "
-                      f"replay of {m['steps']} layer-steps (one untimed replay first); median",
+            "timing": f"{m['warmup']} warm-up layer-steps, then {args.repeats} repeats of a timed graph "
+                      f"replay of {m['steps']} layer-steps, each queued behind an untimed replay of "
+                      f"the same graph; median",
             "repeats": args.repeats,
             "full_ms_repeats": [round(x, 6) for x in m["full"]],
             "partial_ms_repeats": [round(x, 6) for x in m["part"]],

@@ -29,6 +29,9 @@ def command(out=LIB, extra=()):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed-fp32 VALU forms are kept out of the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the kernels' leading arguments (what a workgroup needs before its first loads)
+        # arrive preloaded in SGPRs on gfx950 instead of through a kernel-argument load
+        "-mllvm", "-amdgpu-kernarg-preload-count=14",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(REPO, "include"), "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],

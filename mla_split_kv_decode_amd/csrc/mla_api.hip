@@ -140,7 +140,7 @@ mla_status scratch_of_current_device(void** out) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.6.7 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.7.0 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -444,6 +444,7 @@ mla_status decode_impl(const mla_plan* plan, const void* q, const mla_paged_kv* 
   fill_plan_args(*plan, &pp.plan);
   pp.hidden = hidden;
   pp.nt_parts = partial_nt_parts(plan->max_req_slots);
+  pp.stream_pages = plan->total_pages * (int64_t)mla_page_bytes(kPage, plan->kv_dtype) > kStreamKvBytes;
   if (!out && !out_lse) {
     if (plan->num_wg > 0) {
       hipError_t e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);

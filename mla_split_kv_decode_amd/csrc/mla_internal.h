@@ -125,7 +125,12 @@ struct PartialParams {
   const int32_t* hidden;  // null, or [B][T]: token t of request r does not see the last
                           // hidden[r][t] positions (replaces the causal pattern)
   int32_t nt_parts;       // fp32 parts stored non-temporal (read by the column-chunk merge)
+  int32_t stream_pages;   // one-row-block kernels: page copies with the non-temporal hint
 };
+
+// A layer's KV above this size is streamed past the caches (non-temporal page copies): the
+// memory-side cache (256 MB) could not keep the 24 layers' pools between decode steps.
+constexpr int64_t kStreamKvBytes = int64_t(8) << 20;
 
 // Launch parameters of the LSE merge kernel.
 enum MergeMode : int32_t { MERGE_GENERIC = 0, MERGE_DECODE = 1 };

@@ -297,13 +297,23 @@ struct OperandAddr {
 // `valid_rows` (the unwritten tail of a request's last page) are filled from the last
 // valid row instead: their scores are masked, so only their finiteness matters (a zero
 // softmax weight times a NaN left in the pool would still be NaN).
-template <bool FP8, int NW>
+// STREAM (one-row-block kernels, decided per launch): the copies carry the non-temporal
+// hint.  A page that one workgroup alone reads is then not kept in the caches, so the
+// small data every launch reuses (block table, queries, partial answers) stays resident:
+// long32k 15.93 -> 15.45 us a layer-step, ragged 217 -> 194 us (same-box A/B).  The plan
+// asks for it only when a layer's KV is too large for the memory-side cache to keep the
+// layers' pools between steps (tiny's 24 layers of 1.2 MB stay resident without the hint,
+// 5.70 against 5.96 us); pages that several row groups read from their XCD's L2 keep the
+// default policy (the hint cost dcp_fp8 and spec_verify 3% each).
+template <bool FP8, int NW, bool STREAM = false>
 struct PageCopy {
   using TG = TileGeom<FP8>;
   static constexpr int kPer = (TG::kDmaOps + NW - 1) / NW;
   int src_off[kPer];  // this lane's source offsets within a page, one per operation
   int wave, lane;
-  __device__ __forceinline__ PageCopy(int wave_, int lane_) : wave(wave_), lane(lane_) {
+  bool stream;        // non-temporal copies (STREAM kernels only)
+  __device__ __forceinline__ PageCopy(int wave_, int lane_, bool stream_ = false)
+      : wave(wave_), lane(lane_), stream(stream_) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) src_off[j] = TG::dma_src_offset(block(j) * 64 + lane);
   }
@@ -329,8 +339,12 @@ struct PageCopy {
         if (row >= valid_rows) off -= (row - (valid_rows - 1)) * TG::kRowBytes;
       }
       const uint32_t dst = __builtin_amdgcn_readfirstlane(base + block(j) * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(dst), "v"(off), "s"(src) : "memory", "m0");
+      if (STREAM && stream)  // uniform
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                     :: "s"(dst), "v"(off), "s"(src) : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(dst), "v"(off), "s"(src) : "memory", "m0");
     }
   }
 };
@@ -381,21 +395,26 @@ __device__ __forceinline__ void wait_pages(int n) {
   else wait_vmcnt<0>();
 }
 
-// Every scalar argument a partial-stage prologue needs, fetched in one batch: the compiler
-// would otherwise load some fields lazily inside branches, one memory round trip each,
-// before the first page copy can be issued.
+// The scalars of a partial-stage workgroup.  Those it needs before its first block-table
+// load (which pages, where the table and pool are, whose queries) arrive as the leading
+// kernel arguments, which the library is built to have preloaded into SGPRs with the
+// launch; the rest come from the parameter block, whose loads run meanwhile and are
+// settled (all of them at once, rather than one round trip per use inside a branch) once
+// the table loads are out.
 struct HotArgs {
-  int heads, hgroups, rgroups, mode, nwg, nsplits, plan_n, len0, maxp, batch, qlen, causal, nslots;
+  int heads, hgroups, rgroups, mode, nwg, nsplits, plan_n, len0, maxp, batch, qlen, causal, nslots, stream;
   int64_t total, npages;
   float sscale, vscale;
-  __device__ __forceinline__ explicit HotArgs(const PartialParams& p)
-      : heads(p.num_heads), hgroups(p.head_groups), rgroups(p.row_groups), mode(p.mode), nwg(p.num_wg),
-        nsplits(p.num_splits), plan_n(p.plan.n), len0(p.plan.len[0]), maxp(p.max_pages),
-        batch(p.batch), qlen(p.q_len), causal(p.causal), nslots(p.num_slots),
-        total(p.total_pages), npages(p.num_pages), sscale(p.score_scale), vscale(p.v_scale) {
-    asm volatile("" ::"s"(heads), "s"(hgroups), "s"(rgroups), "s"(mode), "s"(nwg), "s"(nsplits), "s"(plan_n),
-                 "s"(len0), "s"(maxp), "s"(batch), "s"(qlen), "s"(causal), "s"(nslots),
-                 "s"(total), "s"(npages), "s"(sscale), "s"(vscale));
+  __device__ __forceinline__ HotArgs(const PartialParams& p, int nwg_, int rgroups_, int mode_, int plan_n_,
+                                     int total32, int len0_, int maxp_, int heads_)
+      : heads(heads_), hgroups(p.head_groups), rgroups(rgroups_), mode(mode_), nwg(nwg_),
+        nsplits(p.num_splits), plan_n(plan_n_), len0(len0_), maxp(maxp_),
+        batch(p.batch), qlen(p.q_len), causal(p.causal), nslots(p.num_slots), stream(p.stream_pages),
+        total(plan_n_ > 0 ? (int64_t)total32 : p.total_pages), npages(p.num_pages), sscale(p.score_scale),
+        vscale(p.v_scale) {}
+  __device__ __forceinline__ void settle() const {
+    asm volatile("" ::"s"(hgroups), "s"(nsplits), "s"(batch), "s"(qlen), "s"(causal), "s"(nslots),
+                 "s"(stream), "s"(npages), "s"(sscale), "s"(vscale));
   }
 };
 
@@ -524,9 +543,10 @@ __device__ __forceinline__ bool unit_of_block(int nwg, int rgroups, int64_t& w, 
 
 template <bool FP8, int RBW, bool RS, bool F8QK, bool HID, bool NT>
 __device__ __forceinline__ void partial_ks(
-    const PartialParams& p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ part_o, float* __restrict__ part_lse, KSplitSmem<FP8, RBW>& sm) {
+    const PartialParams& p, const HotArgs& args, const uint16_t* __restrict__ q_ptr,
+    const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_lse,
+    KSplitSmem<FP8, RBW>& sm) {
   using C = KSplitCfg<FP8, RBW>;
   using TG = TileGeom<FP8>;
   constexpr int kTiles = C::kTiles, kPer = C::kPer, CT = C::CT, KS = C::KS;
@@ -543,7 +563,6 @@ __device__ __forceinline__ void partial_ks(
   static_assert(!F8QK || (FP8 && RS && KQ == 18), "FP8 QK^T needs the FP8 row split");
   constexpr int NQ = RS ? 1 : RBW;      // row blocks whose queries a wave holds
   constexpr int kEarlyTiles = kTiles - C::kQTiles;  // tiles not used to stage the queries
-  const HotArgs args(p);
   int64_t w;
   int g;
   if (!unit_of_block(args.nwg, args.rgroups, w, g)) return;
@@ -571,7 +590,8 @@ __device__ __forceinline__ void partial_ks(
   int lag_max = 0;
 #pragma unroll
   for (int j = 0; j < RBW; ++j) lag_max = max(lag_max, lag[j]);
-  const PageCopy<FP8, C::NW> copy(wave, lane);
+  // one row block: this workgroup alone reads its pages (non-temporal copies)
+  const PageCopy<FP8, C::NW, RBW == 1> copy(wave, lane, args.stream);
   const OperandAddr<FP8> addr(lrow, lgrp, 4 * wave);  // V^T: output column tiles 4w .. 4w+3
   unsigned char* const tiles = sm.tiles;
   using SM = KSplitSmem<FP8, RBW>;
@@ -636,6 +656,7 @@ __device__ __forceinline__ void partial_ks(
 #pragma unroll
     for (int ti = 0; ti < kTiles; ++ti)
       first_id[ti] = kEarlyId ? *(n > 0 ? trow + pb + min(ti, n - 1) : block_table) : 0;
+    args.settle();
     unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
     typename C::QC(wave, lane)(tiles_lds + kEarlyTiles * TG::kPageBytes, q_ptr + (int64_t)r * args.qlen * args.heads * kDLatent, args.heads,
                                args.hgroups, g * RBW, rb_last);
@@ -1249,20 +1270,24 @@ __device__ __forceinline__ void decode_slots(const MergeParams& p, int64_t grp, 
   }
 }
 
+// The leading arguments (up to the parameter block) are preloaded into SGPRs: the first
+// loads of a merge need nothing else.
+#define MLA_MERGE_LEAD_ARGS                                                                        \
+  const void* __restrict__ lead_part_o, const float* __restrict__ lead_part_lse, int32_t a_rows32,  \
+      int32_t a_nwg, int32_t a_nsplits, int32_t a_mode, int32_t a_plan_n, int32_t a_nparts,          \
+      int32_t a_nslots, int32_t a_len0
+#define MLA_MERGE_LEAD_VALUES(p)                                                                    \
+  (p).part_o, (p).part_lse, (int32_t)(p).rows, (p).num_wg, (p).num_splits, (p).split_mode, (p).plan.n, \
+      (p).num_parts, (p).num_slots, (p).plan.len[0]
+
 template <bool PART_BF16, bool OUT_BF16, bool DECODE>
-__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD_ARGS, MergeParams p) {
   using MG = MergeGeom<PART_BF16>;
   constexpr int kCPT = MG::kCPT, kTPS = MG::kTPS, kSPP = MG::kSPP, kPasses = MG::kPasses;
   __shared__ float sm_m[kMergeWaves];
   __shared__ float sm_acc[kMergeWaves][kTPS][kCPT];
   __shared__ float sm_den[kMergeWaves];
-
-  // scalar arguments of the prologue in one batch (as HotArgs does for the partial stage)
-  const int64_t a_rows = p.rows, a_total = p.total_pages;
-  const int a_nwg = p.num_wg, a_nsplits = p.num_splits, a_mode = p.split_mode, a_plan_n = p.plan.n;
-  const int a_nparts = p.num_parts, a_nslots = p.num_slots, a_len0 = p.plan.len[0];
-  asm volatile("" ::"s"(a_rows), "s"(a_total), "s"(a_nwg), "s"(a_nsplits), "s"(a_mode), "s"(a_plan_n),
-               "s"(a_nparts), "s"(a_nslots), "s"(a_len0));
+  const int64_t a_rows = a_rows32, a_total = p.total_pages;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1296,8 +1321,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
   for (int k = 0; k < kPasses; ++k) {
     const int64_t s = s0 + sl + kSPP * k;
     const bool ok = s < s1;
-    l[k] = ok ? p.part_lse[lse_index(s)] : kNegInf;
-    if (ok) load_piece<PART_BF16>(p.part_o, o_index(s), o[k]);
+    l[k] = ok ? lead_part_lse[lse_index(s)] : kNegInf;
+    if (ok) load_piece<PART_BF16>(lead_part_o, o_index(s), o[k]);
     else {
 #pragma unroll
       for (int c = 0; c < kCPT; ++c) o[k][c] = 0.f;
@@ -1308,7 +1333,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
   inconsistent = inconsistent || dev_len != plan_len;
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) mx = nan_max(mx, l[k]);
-  for (int64_t s = s0 + 256 + tid; s < s1; s += kMergeThreads) mx = nan_max(mx, p.part_lse[lse_index(s)]);
+  for (int64_t s = s0 + 256 + tid; s < s1; s += kMergeThreads) mx = nan_max(mx, lead_part_lse[lse_index(s)]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = nan_max(mx, __shfl_xor(mx, off));
   if (lane == 0) sm_m[wave] = mx;
@@ -1334,9 +1359,9 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
       for (int k = 0; k < kPasses; ++k) {
         const int64_t s = base + sl + kSPP * k;
         if (s >= s1) continue;
-        const float a = exp2_fast((p.part_lse[lse_index(s)] - M) * kLog2e);
+        const float a = exp2_fast((lead_part_lse[lse_index(s)] - M) * kLog2e);
         float v[kCPT];
-        load_piece<PART_BF16>(p.part_o, o_index(s), v);
+        load_piece<PART_BF16>(lead_part_o, o_index(s), v);
 #pragma unroll
         for (int c = 0; c < kCPT; ++c) acc[c] += a * v[c];
         den += a;
@@ -1404,12 +1429,9 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MergeParams p)
 constexpr int kRowSlots = 32;
 
 template <bool PART_BF16, bool OUT_BF16, bool DECODE>
-__global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MergeParams p, int64_t total_rows) {
-  const int64_t a_rows = p.rows, a_total = p.total_pages;
-  const int a_nwg = p.num_wg, a_nsplits = p.num_splits, a_mode = p.split_mode, a_plan_n = p.plan.n;
-  const int a_nparts = p.num_parts, a_nslots = p.num_slots, a_len0 = p.plan.len[0];
-  asm volatile("" ::"s"(a_rows), "s"(a_total), "s"(a_nwg), "s"(a_nsplits), "s"(a_mode), "s"(a_plan_n),
-               "s"(a_nparts), "s"(a_nslots), "s"(a_len0));
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MLA_MERGE_LEAD_ARGS, MergeParams p,
+                                                                      int64_t total_rows) {
+  const int64_t a_rows = a_rows32, a_total = p.total_pages;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t orow = 2 * (int64_t)blockIdx.x + (wave >> 1);
   if (orow >= total_rows) return;  // the whole wave
@@ -1428,17 +1450,17 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MergePara
     else return (s * a_rows + row) * kDV + col;
   };
   // all loads of the row at once: lane k < ns holds LSE of slot s0 + k
-  const float l = lane < ns ? p.part_lse[DECODE ? row * a_nslots + s0 + lane : (s0 + lane) * a_rows + row]
+  const float l = lane < ns ? lead_part_lse[DECODE ? row * a_nslots + s0 + lane : (s0 + lane) * a_rows + row]
                             : kNegInf;
   f32x4 o[kRowSlots];
 #pragma unroll
   for (int k = 0; k < kRowSlots; ++k) {
     if (k < ns) {  // uniform
       if constexpr (PART_BF16) {
-        const bf16x4 b = *(const bf16x4*)((const __bf16*)p.part_o + o_index(s0 + k));
+        const bf16x4 b = *(const bf16x4*)((const __bf16*)lead_part_o + o_index(s0 + k));
         o[k] = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
       } else {
-        o[k] = *(const f32x4*)((const float*)p.part_o + o_index(s0 + k));
+        o[k] = *(const f32x4*)((const float*)lead_part_o + o_index(s0 + k));
       }
     }
   }
@@ -1581,14 +1603,17 @@ static_assert(KSplitCfg<false, 1>::NW * 64 == kPartialThreads, "workgroup size")
 
 // Eight waves, two per SIMD; the page tiles cap residency at one workgroup per compute
 // unit, so each wave may hold up to 256 registers.
+// The leading arguments (up to the parameter block) are the ones preloaded into SGPRs.
 template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
 __global__ __launch_bounds__(kPartialThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
-    PartialParams p, const uint16_t* __restrict__ q_ptr, const uint8_t* __restrict__ pool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    const int32_t* __restrict__ block_table, const uint8_t* __restrict__ pool, const uint16_t* __restrict__ q_ptr,
+    int32_t nwg, int32_t rgroups, int32_t mode, int32_t plan_n, int32_t total32, int32_t len0, int32_t maxp,
+    int32_t heads, PartialParams p, const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
   __shared__ KSplitSmem<FP8, RBW> sm;
-  partial_ks<FP8, RBW, RBW == 2, F8QK, HID, NT>(p, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+  const HotArgs args(p, nwg, rgroups, mode, plan_n, total32, len0, maxp, heads);
+  partial_ks<FP8, RBW, RBW == 2, F8QK, HID, NT>(p, args, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1597,9 +1622,11 @@ namespace {
 
 template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
 void launch_partial_k(const PartialParams& p, hipStream_t stream) {
+  const int32_t total32 = p.plan.n > 0 ? (int32_t)p.total_pages : 0;  // the plan path has P < 2^31
   hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, HID, NT>), dim3(partial_grid(p.num_wg, p.row_groups)),
-                     dim3(kPartialThreads), 0, stream, p, p.q, p.pool, p.block_table,
-                     p.seq_lens, p.part_o, p.part_lse);
+                     dim3(kPartialThreads), 0, stream, p.block_table, p.pool, p.q, p.num_wg, p.row_groups,
+                     p.mode, p.plan.n, total32, p.plan.len[0], p.max_pages, p.num_heads, p, p.seq_lens,
+                     p.part_o, p.part_lse);
 }
 
 template <bool FP8, int RBW, bool F8QK = false>
@@ -1661,7 +1688,8 @@ hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64
     const dim3 grid((unsigned)((total_rows + 1) / 2));
     switch (sel) {
 #define MLA_MERGE_CASE(S, A, B, D) \
-      case S: hipLaunchKernelGGL((mla_merge_rows_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, p, total_rows); break;
+      case S: hipLaunchKernelGGL((mla_merge_rows_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, \
+                                 MLA_MERGE_LEAD_VALUES(p), p, total_rows); break;
       MLA_MERGE_CASE(0, false, false, false)
       MLA_MERGE_CASE(1, false, false, true)
       MLA_MERGE_CASE(2, false, true, false)
@@ -1677,7 +1705,8 @@ hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64
   const dim3 grid((unsigned)(total_rows * kMergeChunks));
   switch (sel) {
 #define MLA_MERGE_CASE(S, A, B, D) \
-    case S: hipLaunchKernelGGL((mla_merge_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, p); break;
+    case S: hipLaunchKernelGGL((mla_merge_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, \
+                               MLA_MERGE_LEAD_VALUES(p), p); break;
     MLA_MERGE_CASE(0, false, false, false)
     MLA_MERGE_CASE(1, false, false, true)
     MLA_MERGE_CASE(2, false, true, false)
