@@ -363,7 +363,7 @@ def main():
             sys.exit("--q-len needs a workload with one history length")
         over = dict(q_len=args.q_len, seq_len=spec["seq_len"] - spec["q_len"] + args.q_len)
     nl = max(1, args.layers)
-    big = args.workload in ("ragged", "spec_verify")
+    big = args.workload in ("ragged", "ragged256", "spec_verify")
     t_gen = time.perf_counter()
     # the two gigabyte-sized workloads get their timing pools on the device; the others
     # use the oracle's generator (also for the CPU baseline)

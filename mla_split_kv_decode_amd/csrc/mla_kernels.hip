@@ -418,12 +418,71 @@ struct HotArgs {
   }
 };
 
+// Device lengths under SPLIT_BALANCED (a batch beyond the plan's argument copy): the page
+// total P and the first request of unit w's page range [gb, ge) with its page prefix, in
+// O(B / threads + log threads) steps.  Thread t sums the pages of requests
+// [t c, (t + 1) c), c = ceil(B / threads); a scan of these sums over the workgroup (wave
+// scans, then the wave totals through `xch`) places every chunk on the page axis, and the
+// one thread whose chunk holds page gb walks it to the request.  Every thread of the
+// workgroup calls it (two barriers); the results are uniform and returned in SGPRs.
+// `xch`: at least NW + 2 int64 of LDS, free until the caller's next barrier.
+template <int NW>
+__device__ __forceinline__ bool device_unit_start(const int32_t* __restrict__ seq_lens, int batch, int maxp,
+                                                  int64_t w, int64_t nwg, int64_t total,
+                                                  int64_t* __restrict__ xch, int& r_first,
+                                                  int64_t& pre_first, int64_t& gb, int64_t& ge) {
+  constexpr int kThreads = NW * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = (batch + kThreads - 1) / kThreads;
+  const int r0 = min(tid * chunk, batch), r1 = min(r0 + chunk, batch);
+  int64_t own = 0;
+  for (int r = r0; r < r1; ++r) own += pages_of(seq_lens[r], maxp);
+  int64_t inc = own;  // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
+  }
+  if (lane == 63) xch[wave] = inc;
+  __syncthreads();
+  int64_t P = 0, before = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int64_t t = xch[v];
+    before += v < wave ? t : 0;
+    P += t;
+  }
+  // lengths that disagree with the plan's total: no piece (the merge writes NaN)
+  if (P == 0 || P != total) return false;
+  gb = balanced_start(w, P, nwg);
+  ge = balanced_start(w + 1, P, nwg);
+  int64_t pre = before + inc - own;  // pages of the requests before this thread's chunk
+  if (own > 0 && pre <= gb && gb < pre + own) {
+    for (int r = r0; r < r1; ++r) {
+      const int pr = pages_of(seq_lens[r], maxp);
+      if (pre + pr > gb) {
+        xch[NW] = r;
+        xch[NW + 1] = pre;
+        break;
+      }
+      pre += pr;
+    }
+  }
+  __syncthreads();
+  r_first = __builtin_amdgcn_readfirstlane((int)xch[NW]);
+  const int64_t pf = xch[NW + 1];
+  pre_first = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(pf >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)pf));
+  return true;
+}
+
 // The pieces of work unit w (mla_internal.h): run(r, first page, end page, slot, L) for
-// each, from the plan's lengths in the arguments when present, else from seq_lens.
-template <class F>
+// each, from the plan's lengths in the arguments when present, else from seq_lens (then
+// every thread of the workgroup must call it; `xch` as for device_unit_start).
+template <int NW, class F>
 __device__ __forceinline__ void for_each_piece(const PartialParams& p, const HotArgs& a,
                                                const int32_t* __restrict__ seq_lens, int64_t w,
-                                               F&& run_piece) {
+                                               int64_t* __restrict__ xch, F&& run_piece) {
   const bool use_plan = a.plan_n > 0;
   if (a.mode == SPLIT_FIXED) {
     const int S = a.nsplits;
@@ -446,14 +505,10 @@ __device__ __forceinline__ void for_each_piece(const PartialParams& p, const Hot
       run_piece(r, (int)(lo - pre), (int)(hi - pre), w + r, L);
     }
   } else {
-    int64_t P = 0;
-    for (int r = 0; r < a.batch; ++r) P += pages_of(seq_lens[r], a.maxp);
-    // Device lengths that disagree with the plan's: no piece is computed and the merge
-    // writes NaN (the split below would not match the merge's slot ranges).
-    if (P == 0 || P != a.total) return;
-    const int64_t gb = balanced_start(w, P, a.nwg), ge = balanced_start(w + 1, P, a.nwg);
-    int64_t pre = 0;
-    for (int r = 0; r < a.batch && pre < ge; ++r) {
+    int r;
+    int64_t pre, gb, ge;
+    if (!device_unit_start<NW>(seq_lens, a.batch, a.maxp, w, a.nwg, a.total, xch, r, pre, gb, ge)) return;
+    for (; r < a.batch && pre < ge; ++r) {
       const int L = max(seq_lens[r], 0);
       const int pr = pages_of(L, a.maxp);
       const int64_t lo = gb > pre ? gb : pre;
@@ -1187,7 +1242,10 @@ __device__ __forceinline__ void partial_ks(
     barrier_lds();  // tiles and exchange buffers are reused by the next piece
   };
 
-  for_each_piece(p, args, seq_lens, w, run_piece);
+  // the cross-wave exchange of the device-length scan borrows the denominator buffer, which
+  // the first piece writes only after several barriers
+  static_assert(sizeof(sm.red2) >= (C::NW + 2) * sizeof(int64_t), "scan exchange");
+  for_each_piece<C::NW>(p, args, seq_lens, w, reinterpret_cast<int64_t*>(&sm.red2[0][0]), run_piece);
 }
 
 // ------------------------------------------------------------------- merge
@@ -1226,13 +1284,52 @@ __device__ __forceinline__ void load_piece(const void* base, int64_t idx, float 
   }
 }
 
+// Device lengths under SPLIT_BALANCED (a batch beyond the plan's argument copy): the page
+// total P, the page prefix pre0 of request g0 and the page counts pr0, pr1 of requests g0
+// and g0 + 1, by a reduction of seq_lens over the workgroup (thread t takes requests
+// t, t + kMergeThreads, ...).  Every thread of the workgroup calls it (one barrier).
+struct DevicePages {
+  int64_t P, pre0, pr0, pr1;
+};
+__device__ __forceinline__ DevicePages device_pages(const int32_t* __restrict__ seq_lens, int batch,
+                                                    int maxp, int64_t g0,
+                                                    int64_t (&xs)[kMergeWaves][4]) {
+  int64_t v[4] = {0, 0, 0, 0};
+  for (int r = threadIdx.x; r < batch; r += kMergeThreads) {
+    const int pg = pages_of(seq_lens[r], maxp);
+    v[0] += pg;
+    v[1] += r < g0 ? pg : 0;
+    v[2] += r == g0 ? pg : 0;
+    v[3] += r == g0 + 1 ? pg : 0;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v[k] += __shfl_xor(v[k], off);
+    if (lane == 0) xs[wave][k] = v[k];
+  }
+  __syncthreads();
+  DevicePages d{0, 0, 0, 0};
+#pragma unroll
+  for (int wv = 0; wv < kMergeWaves; ++wv) {
+    d.P += xs[wv][0];
+    d.pre0 += xs[wv][1];
+    d.pr0 += xs[wv][2];
+    d.pr1 += xs[wv][3];
+  }
+  return d;
+}
+
 // Slot range [s0, s1) of request grp's partial answers.  Under SPLIT_BALANCED every work
 // unit owns at least one page (W <= P), so every slot in the range holds a piece.  On the
 // plan path the device length (a vector load, waited for only where it is compared, after
 // the partial answers have been loaded) must equal the plan's: the caller compares
-// dev_len with plan_len.
+// dev_len with plan_len.  Device lengths under SPLIT_BALANCED come in `dp` (device_pages
+// with g0 = grp or grp - 1).
 __device__ __forceinline__ void decode_slots(const MergeParams& p, int64_t grp, int plan_n, int mode,
                                              int nsplits, int nwg, int64_t total, int len0,
+                                             const DevicePages& dp, int64_t g0,
                                              int64_t& s0, int64_t& s1, bool& inconsistent,
                                              int& dev_len, int& plan_len) {
   if (plan_n == 1) {  // one request
@@ -1255,17 +1352,12 @@ __device__ __forceinline__ void decode_slots(const MergeParams& p, int64_t grp, 
     s0 = grp * nsplits;
     s1 = s0 + nsplits;
   } else {
-    int64_t P = 0, pre = 0, pr = 0;
-    for (int r = 0; r < p.batch; ++r) {
-      const int pg = pages_of(p.seq_lens[r], p.max_pages);
-      if (r < grp) pre += pg;
-      if (r == grp) pr = pg;
-      P += pg;
-    }
-    inconsistent = P != p.total_pages;
+    const bool second = grp != g0;
+    const int64_t pre = second ? dp.pre0 + dp.pr0 : dp.pre0, pr = second ? dp.pr1 : dp.pr0;
+    inconsistent = dp.P != total;
     if (pr > 0 && !inconsistent) {
-      s0 = balanced_wg_of(pre, P, p.num_wg) + grp;
-      s1 = balanced_wg_of(pre + pr - 1, P, p.num_wg) + grp + 1;
+      s0 = balanced_wg_of(pre, dp.P, nwg) + grp;
+      s1 = balanced_wg_of(pre + pr - 1, dp.P, nwg) + grp + 1;
     }
   }
 }
@@ -1287,6 +1379,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
   __shared__ float sm_m[kMergeWaves];
   __shared__ float sm_acc[kMergeWaves][kTPS][kCPT];
   __shared__ float sm_den[kMergeWaves];
+  __shared__ int64_t sm_xs[kMergeWaves][4];
   const int64_t a_rows = a_rows32, a_total = p.total_pages;
 
   const int tid = threadIdx.x;
@@ -1302,8 +1395,15 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
   int64_t s0 = 0, s1 = 0;
   bool inconsistent = false;
   int dev_len = 0, plan_len = 0;
-  if constexpr (!DECODE) s1 = a_nparts;
-  else decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, s0, s1, inconsistent, dev_len, plan_len);
+  DevicePages dp{0, 0, 0, 0};
+  if constexpr (!DECODE) {
+    s1 = a_nparts;
+  } else {
+    if (a_plan_n == 0 && a_mode == SPLIT_BALANCED)  // uniform over the workgroup
+      dp = device_pages(p.seq_lens, p.batch, p.max_pages, grp, sm_xs);
+    decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, dp, grp, s0, s1, inconsistent,
+                 dev_len, plan_len);
+  }
   const int64_t col = (int64_t)chunk * kMergeCols + cp * kCPT;
   auto o_index = [&](int64_t s) -> int64_t {
     if constexpr (DECODE) return ((row * kMergeChunks + chunk) * a_nslots + s) * kMergeCols + cp * kCPT;
@@ -1434,16 +1534,24 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MLA_MERGE
   const int64_t a_rows = a_rows32, a_total = p.total_pages;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t orow = 2 * (int64_t)blockIdx.x + (wave >> 1);
-  if (orow >= total_rows) return;  // the whole wave
   const int col = (wave & 1) * 256 + lane * 4;
   const int64_t grp = (int64_t)((uint32_t)orow / (uint32_t)a_rows);  // rows * groups < 2^31
   const int64_t row = orow - grp * a_rows;
+  // the block's two rows belong to request g0 or g0 + 1
+  const int64_t g0 = (int64_t)((uint32_t)(2 * blockIdx.x) / (uint32_t)a_rows);
+  DevicePages dp{0, 0, 0, 0};
+  if (DECODE && a_plan_n == 0 && a_mode == SPLIT_BALANCED) {  // uniform over the workgroup
+    __shared__ int64_t sm_xs[kMergeWaves][4];
+    dp = device_pages(p.seq_lens, p.batch, p.max_pages, g0, sm_xs);
+  }
+  if (orow >= total_rows) return;  // the whole wave
 
   int64_t s0 = 0, s1 = 0;
   bool inconsistent = false;
   int dev_len = 0, plan_len = 0;
   if constexpr (!DECODE) s1 = a_nparts;
-  else decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, s0, s1, inconsistent, dev_len, plan_len);
+  else decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, dp, g0, s0, s1, inconsistent,
+                    dev_len, plan_len);
   const int ns = (int)(s1 - s0);
   auto o_index = [&](int64_t s) -> int64_t {
     if constexpr (DECODE) return ((row * kMergeChunks + (col >> 5)) * a_nslots + s) * kMergeCols + (col & 31);

@@ -16,6 +16,8 @@ Workloads (the shapes the source pages discuss; see the module-level table
                   (the partition count of the AITER assembly policy in the
                   pages' section 4);
 * ``ragged``      batch 64, 16 heads, lengths uniform in [1024, 32768];
+* ``ragged256``   the same with 256 requests (a large serving batch: past the 64
+                  requests whose lengths travel in the kernel arguments);
 * ``dcp_fp8``     batch 8, 96 heads (all heads on one DCP8 shard), 17,750
                   local positions (142,000 / 8, the conversation of the pages'
                   section 1 payload estimate), FP8 E4M3FN pool;
@@ -55,6 +57,9 @@ CONFIGS = {
                     shuffled=True, num_splits=0),
     "spec_verify": dict(batch=8, q_len=4, num_heads=16, seq_len=131072 + 4, kv_format="bf16",
                         shuffled=True, num_splits=16),
+    # (after the five workloads above, whose seeds are their positions 1 .. 5)
+    "ragged256": dict(batch=256, q_len=1, num_heads=16, seq_len_range=(1024, 32768),
+                      kv_format="bf16", shuffled=True, num_splits=0),
 }
 
 
@@ -137,7 +142,7 @@ def make_pool(rng, seq_lens, block_table, num_pages, kv_format, page_size=PAGE_S
         return pool, np.float32(1.0)
     if kv_format == "fp8_e4m3fn":
         xs = [rng.standard_normal((int(L), D_LATENT), dtype=np.float32) for L in seq_lens]
-        max_abs = max(float(np.abs(x).max()) for x in xs)
+        max_abs = max((float(np.abs(x).max()) for x in xs if x.size), default=1.0)  # empty requests
         sigma = e4m3fn_scale(max_abs)
         pool = np.full((num_pages, page_size, D_LATENT), E4M3FN_NAN, dtype=np.uint8)
         for r, x in enumerate(xs):

@@ -798,6 +798,44 @@ def test_large_batch_device_lengths_path():
     assert torch.isnan(lse).all()
 
 
+LARGE_BATCH = [
+    # batch, q_len, heads, kv, splits, lengths
+    (300, 1, 16, "bf16", 0, "short"),       # one request per scan thread, row-wise merge
+    (600, 1, 16, "bf16", 0, "tiny"),        # two requests per scan thread
+    (90, 1, 7, "bf16", 0, "short"),         # odd row count: merge blocks straddle requests
+    (80, 1, 16, "bf16", 0, "one_long"),     # > 32 parts for one request: column-chunk merge
+    (100, 2, 16, "fp8_e4m3fn", 0, "short"),
+    (130, 1, 48, "bf16", 0, "short"),       # several row groups
+    (100, 1, 16, "bf16", 3, "short"),       # fixed splits
+]
+
+
+@pytest.mark.parametrize("case", LARGE_BATCH, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}{c[3]}s{c[4]}{c[5]}")
+def test_large_batch_device_lengths_full(case):
+    """Past 64 requests every workgroup finds its pages and slots from the device lengths
+    by a workgroup scan: every request of the batch matches the oracle, including the
+    shortest requests the plan accepts, requests whose pages span several units and
+    requests split between the two rows of a merge block."""
+    B, T, H, kv, splits, mix = case
+    rng = np.random.default_rng(605 + B + H)
+    lens = rng.integers(T, 130 if mix == "tiny" else 400, size=B)
+    lens[1], lens[2], lens[-1] = T, 65, 64
+    if mix == "one_long":
+        lens[B // 3] = 6000
+    wl = wk.make_workload(None, seed=605 + B, batch=B, q_len=T, num_heads=H, seq_lens=list(lens),
+                          kv_format=kv, shuffled=True)
+    # Requests of a few positions give outputs of magnitude above 4, where one bf16 rounding
+    # alone can reach 2^-6: the bar applies to the fp32 result, and the bf16 output must be
+    # that result rounded to nearest even.
+    o, l = run_gpu(wl, num_splits=splits, out_dtype="fp32")
+    o_ref, l_ref = run_oracle(wl)
+    compare(wl, o, l, o_ref, l_ref, f"{B} requests, device lengths")
+    o16, l16 = run_gpu(wl, num_splits=splits)
+    import torch
+    rne = torch.from_numpy(o.astype(np.float32)).bfloat16().double().numpy()
+    assert np.array_equal(o16, rne) and np.array_equal(l16, l)
+
+
 # ------------------------------------------------------------ cache append
 
 def _append_inputs(kv_format, seed, batch, q_len, seq_lens, special=False):
