@@ -4,6 +4,7 @@
                     [--splits auto|N] [--layers 24] [--repeats R]
                     [--no-cpu-baseline] [--no-other-workloads]
     python bench.py --read-ceiling [--workload long32k]
+    python bench.py --lds-reserve 0,65536,98304 [--workload ragged256]
 
 A step is one MLA layer-step: the partial-attention kernel plus the LSE merge kernel
 for the whole batch of one layer, on one stream.  Consecutive steps rotate through
@@ -25,7 +26,9 @@ arithmetic intensity is past the ridge (the 96-head DCP shard).  `cpu_baseline` 
 the fp64 oracle on a bounded sample of the same workload on all host cores and on one
 thread.  `detail.workloads` holds a compact line for each other named workload (pools
 drawn on the device), and `--read-ceiling` times a plain read of the same rotated pools
-(the floor of any single launch that streams them) and an empty launch.
+(the floor of any single launch that streams them) and an empty launch.  `--lds-reserve`
+runs the residency experiment: the same decode with unused LDS reserved by every merge
+workgroup (the MLA_LDS_RESERVE knob read at plan creation), one timing per reserve.
 """
 
 import argparse
@@ -76,6 +79,10 @@ def parse():
     ap.add_argument("--read-ceiling", action="store_true",
                     help="time a plain read of the workload's rotated pools (registers and LDS "
                          "copies) and an empty launch, instead of the decode")
+    ap.add_argument("--lds-reserve", default="",
+                    help="comma-separated byte counts: time the decode with each as unused LDS "
+                         "per merge workgroup (same binary; the residency experiment), instead "
+                         "of the default line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -307,6 +314,48 @@ def read_ceiling(args, mb, wk, wl, nl):
     }), flush=True)
 
 
+# Static LDS of the merge kernels (largest variant, from the kernel metadata), the LDS of
+# one compute unit and the allocation granule.
+MERGE_STATIC_LDS = 672
+CU_LDS = 160 * 1024
+LDS_GRANULE = 1280
+
+
+def lds_residency(args, mb, wk, wl, splits, nl, big):
+    """The residency experiment: the same decode with each reserve of unused LDS per merge
+    workgroup.  A reserve that lowers the number of merge workgroups a compute unit can
+    hold but leaves the time unchanged shows the extra resident workgroups do not matter
+    for this workload."""
+    import os
+
+    runs = []
+    for b in [int(x) for x in args.lds_reserve.split(",") if x.strip()]:
+        os.environ["MLA_LDS_RESERVE"] = str(b)
+        try:
+            m = measure(args, mb, wk, wl, splits, nl, args.fp8_qk, device_pools=big)
+        finally:
+            del os.environ["MLA_LDS_RESERVE"]
+        alloc = -(-(MERGE_STATIC_LDS + b) // LDS_GRANULE) * LDS_GRANULE
+        runs.append({
+            "lds_reserve_bytes": b,
+            "merge_workgroups_per_cu_lds_limit": CU_LDS // alloc,
+            "us_per_layer_step": round(m["ms"] * 1e3, 3),
+            "partial_us": round(m["ms_part"] * 1e3, 3),
+            "merge_and_gap_us": round((m["ms"] - m["ms_part"]) * 1e3, 3),
+            "full_ms_repeats": [round(x, 6) for x in m["full"]],
+        })
+        print(f"[bench] lds reserve {b}: {runs[-1]['us_per_layer_step']} us/layer-step", file=sys.stderr,
+              flush=True)
+    print(json.dumps({
+        "metric": "decode µs/layer-step with unused LDS reserved per merge workgroup (residency experiment)",
+        "unit": "us", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": describe(wl, splits), "layers_rotated": nl},
+        "steps": args.steps, "warmup": args.warmup, "repeats": args.repeats,
+        "merge_static_lds_bytes": MERGE_STATIC_LDS, "runs": runs,
+        "library": mb.version(),
+    }), flush=True)
+
+
 def bench_append(args, wl, mb, st, nl):
     """µs per mla_kv_append of the step's B x T new latents into one layer's pool, alone
     and followed by that layer's decode."""
@@ -373,6 +422,9 @@ def main():
 
     if args.read_ceiling:
         read_ceiling(args, mb, wk, wl, nl)
+        return
+    if args.lds_reserve:
+        lds_residency(args, mb, wk, wl, splits, nl, big)
         return
     if args.append:
         st = setup(mb, wk, wl, splits, nl, args.fp8_qk, device_pools=big)

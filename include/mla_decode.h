@@ -142,6 +142,12 @@ typedef struct mla_plan mla_plan; /* opaque, host memory */
  *   num_cus        compute units to fill; 0 = query the current device
  *   plan           out: new plan, release with mla_plan_destroy
  *   workspace_bytes out: device workspace size mla_decode_splitkv needs with it
+ * Residency experiment (Kimi K3 on MI355X, "Technical notes": reserve unused LDS to
+ * cross an occupancy threshold with the same kernel binary, then compare times): when
+ * the environment variable MLA_LDS_RESERVE holds a byte count at plan creation, every
+ * merge workgroup of the plan's decodes reserves that much unused LDS (clamped to
+ * [0, 131072]; results are unchanged, only how many merge workgroups a compute unit
+ * holds at once).  Unset, no LDS is reserved.
  */
 mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_lens_host,
                            int32_t page_size, int32_t kv_dtype, int32_t num_cus,

@@ -19,7 +19,8 @@ namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, bool fp8_qk, hipStream_t stream);
 bool partial_nt_parts(int64_t max_row_slots);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
-                        int max_row_slots, hipStream_t stream);
+                        int max_row_slots, uint32_t lds_reserve, hipStream_t stream);
+constexpr long long kMaxLdsReserve = 128 * 1024;
 size_t partial_lds_size(bool fp8, int rbw);
 hipError_t launch_read_reference(const void* buf, int64_t bytes, int mode, uint32_t* sink, hipStream_t stream);
 hipError_t launch_kv_append(void* pool, int64_t num_pages, bool fp8, const int32_t* block_table,
@@ -48,6 +49,7 @@ struct mla_plan {
   int32_t max_req_pages;  // largest ceil(seq_len / page) of a request
   int32_t max_req_slots;  // most partial answers of one request
   size_t o_offset, o_bytes, lse_offset, workspace_bytes;
+  uint32_t lds_reserve;   // unused LDS per merge workgroup (residency experiment)
   std::vector<int32_t> seq_lens;  // host copy, for get_work only
 };
 
@@ -239,6 +241,11 @@ mla_status mla_plan_create(const mla_decode_shape* shape, const int32_t* seq_len
   pl->total_pages = total_pages;
   pl->max_req_pages = max_req_pages;
   pl->seq_lens.assign(seq_lens_host, seq_lens_host + s.batch);
+  pl->lds_reserve = 0;
+  if (const char* env = getenv("MLA_LDS_RESERVE")) {
+    const long long v = strtoll(env, nullptr, 10);
+    pl->lds_reserve = (uint32_t)(v < 0 ? 0 : v > kMaxLdsReserve ? kMaxLdsReserve : v);
+  }
   const bool fp8 = kv_dtype == MLA_FP8_E4M3FN;
   int64_t wg, slots;
   if (s.num_splits > 0) {
@@ -474,7 +481,7 @@ mla_status decode_impl(const mla_plan* plan, const void* q, const mla_paged_kv* 
     e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);
     if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "partial launch: %s", hipGetErrorString(e));
   }
-  e = launch_merge(mp, false, true, (int64_t)s.batch * plan->rows, plan->max_req_slots, st);
+  e = launch_merge(mp, false, true, (int64_t)s.batch * plan->rows, plan->max_req_slots, plan->lds_reserve, st);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -543,7 +550,7 @@ mla_status mla_merge_lse(const void* part_o, int32_t part_dtype, const float* pa
   mp.rows = rows;
   mp.out_bf16 = out_dtype == MLA_BF16;
   mp.num_parts = num_parts;
-  hipError_t e = launch_merge(mp, part_dtype == MLA_BF16, false, rows, num_parts, (hipStream_t)stream);
+  hipError_t e = launch_merge(mp, part_dtype == MLA_BF16, false, rows, num_parts, 0, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_DEVICE, "merge launch: %s", hipGetErrorString(e));
   return ok();
 }

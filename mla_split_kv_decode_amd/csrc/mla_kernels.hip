@@ -1789,14 +1789,15 @@ bool partial_nt_parts(int64_t max_row_slots) {
   return max_row_slots > kRowSlots;
 }
 
+// lds_reserve: unused dynamic LDS per workgroup (the residency experiment), 0 normally.
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
-                        int max_row_slots, hipStream_t stream) {
+                        int max_row_slots, uint32_t lds_reserve, hipStream_t stream) {
   const int sel = (part_bf16 ? 4 : 0) + (p.out_bf16 ? 2 : 0) + (decode ? 1 : 0);
   if (max_row_slots <= kRowSlots) {
     const dim3 grid((unsigned)((total_rows + 1) / 2));
     switch (sel) {
 #define MLA_MERGE_CASE(S, A, B, D) \
-      case S: hipLaunchKernelGGL((mla_merge_rows_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, \
+      case S: hipLaunchKernelGGL((mla_merge_rows_kernel<A, B, D>), grid, dim3(kMergeThreads), lds_reserve, stream, \
                                  MLA_MERGE_LEAD_VALUES(p), p, total_rows); break;
       MLA_MERGE_CASE(0, false, false, false)
       MLA_MERGE_CASE(1, false, false, true)
@@ -1813,7 +1814,7 @@ hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64
   const dim3 grid((unsigned)(total_rows * kMergeChunks));
   switch (sel) {
 #define MLA_MERGE_CASE(S, A, B, D) \
-    case S: hipLaunchKernelGGL((mla_merge_kernel<A, B, D>), grid, dim3(kMergeThreads), 0, stream, \
+    case S: hipLaunchKernelGGL((mla_merge_kernel<A, B, D>), grid, dim3(kMergeThreads), lds_reserve, stream, \
                                MLA_MERGE_LEAD_VALUES(p), p); break;
     MLA_MERGE_CASE(0, false, false, false)
     MLA_MERGE_CASE(1, false, false, true)

@@ -836,6 +836,20 @@ def test_large_batch_device_lengths_full(case):
     assert np.array_equal(o16, rne) and np.array_equal(l16, l)
 
 
+@pytest.mark.parametrize("reserve", [65536, 131072])
+def test_lds_reserve_leaves_results_unchanged(monkeypatch, reserve):
+    """The residency experiment's knob only reserves unused LDS in the merge workgroups:
+    the outputs are bitwise those of a plan made without it (row-wise and column-chunk
+    merges)."""
+    for lens in ([700, 70, 1300], [6000]):
+        wl = wk.make_workload(None, seed=606, batch=len(lens), q_len=1, num_heads=16, seq_lens=lens)
+        o0, l0 = run_gpu(wl, num_splits=0)
+        monkeypatch.setenv("MLA_LDS_RESERVE", str(reserve))
+        o1, l1 = run_gpu(wl, num_splits=0)
+        monkeypatch.delenv("MLA_LDS_RESERVE")
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
 # ------------------------------------------------------------ cache append
 
 def _append_inputs(kv_format, seed, batch, q_len, seq_lens, special=False):
