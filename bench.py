@@ -51,7 +51,10 @@ RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312
 # the copy-kernel calibration factors (profiles/<kernel>_<workload>.md), keyed by
 # (workload, splits, library version): a kernel change bumps the version, so `traffic`
 # reads null until the counters are taken again.
-TRAFFIC = {}
+TRAFFIC = {
+    ("long32k", 0, "mla_split_kv_decode_amd 0.7.1 (gfx950)"): {
+        "fetch_kib": 18600.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
+}
 
 
 def parse():

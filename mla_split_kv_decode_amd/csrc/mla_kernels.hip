@@ -1231,7 +1231,31 @@ __device__ __forceinline__ void partial_ks(
         oscale = __builtin_nanf("");
         lse = __builtin_nanf("");
       }
-      if (head_ok[j]) {
+      if constexpr (NT) {
+        // Whole 128-byte lines per store instruction.  A lane holds 4 columns of each half of
+        // a 32-column line of its row (tiles ct = 2k and 2k + 1); lanes lrow and lrow ^ 8
+        // trade one half, so that the first store writes the whole lines of rows 0-7 of the
+        // block and the second those of rows 8-15 (eight lanes a line) instead of every
+        // store writing half lines of all 16 rows.
+        const bool lo = lrow < 8;
+        const int head = orow[j] - tok[j] * args.heads;
+        const bool mate_ok = g * RBW + j <= rb_last && (head ^ 8) < args.heads;
+        const int64_t mate_row = orow[j] + (lo ? 8 : -8);
+#pragma unroll
+        for (int ct = 0; ct < CT; ct += 2) {
+          const f32x4 a = acc[j][ct] * oscale, b = acc[j][ct + 1] * oscale;
+          const f32x4 give = lo ? b : a;
+          f32x4 got;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) got[e] = __shfl_xor(give[e], 8);
+          const int c0 = 64 * wave + 16 * ct + 4 * lgrp;  // a's columns; b's are c0 + 16
+          if (lo ? head_ok[j] : mate_ok)
+            store_partial<true>(part_o, lo ? orow[j] : mate_row, lo ? c0 : c0 + 16, args.nslots, slot, lo ? a : got);
+          if (lo ? mate_ok : head_ok[j])
+            store_partial<true>(part_o, lo ? mate_row : orow[j], lo ? c0 : c0 + 16, args.nslots, slot, lo ? got : b);
+        }
+        if (head_ok[j] && wave == 0 && lgrp == 0) part_lse[(int64_t)orow[j] * args.nslots + slot] = lse;
+      } else if (head_ok[j]) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
           store_partial<NT>(part_o, orow[j], 64 * wave + 16 * ct + 4 * lgrp, args.nslots, slot,
