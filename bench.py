@@ -51,10 +51,23 @@ RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312
 # the copy-kernel calibration factors (profiles/<kernel>_<workload>.md), keyed by
 # (workload, splits, library version): a kernel change bumps the version, so `traffic`
 # reads null until the counters are taken again.
+_V071 = "mla_split_kv_decode_amd 0.7.1 (gfx950)"
 TRAFFIC = {
-    ("long32k", 0, "mla_split_kv_decode_amd 0.7.1 (gfx950)"): {
-        "fetch_kib": 18600.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
+    ("long32k", 0, _V071): {"fetch_kib": 18600.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
+    ("tiny", 0, _V071): {"fetch_kib": 738.5, "fetch_factor": 2.000, "write_kib": 520.0, "write_factor": 1.000},
+    ("ragged", 0, _V071): {"fetch_kib": 566973.7, "fetch_factor": 2.000, "write_kib": 10315.1, "write_factor": 1.000},
+    ("spec_verify", 0, _V071): {"fetch_kib": 592338.5, "fetch_factor": 2.000, "write_kib": 16648.9,
+                                "write_factor": 1.000},
+    ("dcp_fp8", 0, _V071): {"fetch_kib": 43571.1, "fetch_factor": 2.000, "write_kib": 15606.7, "write_factor": 1.000},
 }
+
+
+def traffic_of(name, splits, version):
+    """Calibrated HBM bytes per partial-kernel launch from the counters above, or None."""
+    tr = TRAFFIC.get((name, splits, version))
+    if not tr:
+        return None
+    return int(1024 * (tr["fetch_kib"] * tr["fetch_factor"] + tr["write_kib"] * tr["write_factor"]))
 
 
 def parse():
@@ -257,7 +270,7 @@ def measure(args, mb, wk, wl, splits, nl, fp8_qk=False, device_pools=False, step
     return res
 
 
-def compact_line(wl, splits, m):
+def compact_line(wl, splits, m, version):
     kv_b = wk_kv_bytes(wl)
     flops = wk_flops(wl)
     return {
@@ -266,7 +279,7 @@ def compact_line(wl, splits, m):
         "GBps": round(kv_b / (m["ms"] * 1e-3) / 1e9, 2),
         "pct_of_8TBs": round(100 * kv_b / (m["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "partial_us": round(m["ms_part"] * 1e3, 3),
-        "roofline": roofline_of(kv_b, flops, m["ms_part"], None),
+        "roofline": roofline_of(kv_b, flops, m["ms_part"], traffic_of(wl.name, splits, version)),
         "steps": m["steps"], "warmup": m["warmup"], "repeats": len(m["full"]),
         "units": m["units"], "row_groups": m["row_groups"], "parts": m["parts"],
         "data": "synthetic (pools drawn on the device)",
@@ -439,10 +452,7 @@ def main():
     flops = wk.attention_flops(wl.seq_lens, wl.q_len, wl.num_heads, wl.causal)
     ms, ms_part = m["ms"], m["ms_part"]
     gbs = kv_b / (ms * 1e-3) / 1e9
-    traffic = None
-    tr = None if args.fp8_qk else TRAFFIC.get((wl.name, splits, mb.version()))
-    if tr:
-        traffic = int(1024 * (tr["fetch_kib"] * tr["fetch_factor"] + tr["write_kib"] * tr["write_factor"]))
+    traffic = None if args.fp8_qk or args.q_len else traffic_of(wl.name, splits, mb.version())
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -492,7 +502,7 @@ def main():
             st_o = max(4 * nlo, 48) if name in ("ragged", "spec_verify") else args.steps
             mo = measure(args, mb, wk, other, 0, nlo, device_pools=True, steps=st_o,
                          warmup=min(args.warmup, st_o))
-            lines[name] = compact_line(other, 0, mo)
+            lines[name] = compact_line(other, 0, mo, mb.version())
             print(f"[bench] {name}: {lines[name]['us_per_layer_step']} us/layer-step", file=sys.stderr,
                   flush=True)
         res["detail"]["workloads"] = lines
