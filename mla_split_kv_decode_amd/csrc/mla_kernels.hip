@@ -1310,16 +1310,18 @@ __device__ __forceinline__ void load_piece(const void* base, int64_t idx, float 
 
 // Device lengths under SPLIT_BALANCED (a batch beyond the plan's argument copy): the page
 // total P, the page prefix pre0 of request g0 and the page counts pr0, pr1 of requests g0
-// and g0 + 1, by a reduction of seq_lens over the workgroup (thread t takes requests
-// t, t + kMergeThreads, ...).  Every thread of the workgroup calls it (one barrier).
+// and g0 + 1, by a reduction of seq_lens over the workgroup's NWAVES waves (thread t takes
+// requests t, t + 64 NWAVES, ...).  Every thread of the workgroup calls it (one barrier
+// when there are several waves).
 struct DevicePages {
   int64_t P, pre0, pr0, pr1;
 };
+template <int NWAVES>
 __device__ __forceinline__ DevicePages device_pages(const int32_t* __restrict__ seq_lens, int batch,
                                                     int maxp, int64_t g0,
-                                                    int64_t (&xs)[kMergeWaves][4]) {
+                                                    int64_t (&xs)[NWAVES][4]) {
   int64_t v[4] = {0, 0, 0, 0};
-  for (int r = threadIdx.x; r < batch; r += kMergeThreads) {
+  for (int r = threadIdx.x; r < batch; r += 64 * NWAVES) {
     const int pg = pages_of(seq_lens[r], maxp);
     v[0] += pg;
     v[1] += r < g0 ? pg : 0;
@@ -1331,12 +1333,13 @@ __device__ __forceinline__ DevicePages device_pages(const int32_t* __restrict__ 
   for (int k = 0; k < 4; ++k) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v[k] += __shfl_xor(v[k], off);
-    if (lane == 0) xs[wave][k] = v[k];
+    if (NWAVES > 1 && lane == 0) xs[wave][k] = v[k];
   }
+  if constexpr (NWAVES == 1) return DevicePages{v[0], v[1], v[2], v[3]};
   __syncthreads();
   DevicePages d{0, 0, 0, 0};
 #pragma unroll
-  for (int wv = 0; wv < kMergeWaves; ++wv) {
+  for (int wv = 0; wv < NWAVES; ++wv) {
     d.P += xs[wv][0];
     d.pre0 += xs[wv][1];
     d.pr0 += xs[wv][2];
@@ -1424,7 +1427,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
     s1 = a_nparts;
   } else {
     if (a_plan_n == 0 && a_mode == SPLIT_BALANCED)  // uniform over the workgroup
-      dp = device_pages(p.seq_lens, p.batch, p.max_pages, grp, sm_xs);
+      dp = device_pages<kMergeWaves>(p.seq_lens, p.batch, p.max_pages, grp, sm_xs);
     decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, dp, grp, s0, s1, inconsistent,
                  dev_len, plan_len);
   }
@@ -1546,29 +1549,31 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
 
 // Row-wise merge, for plans whose rows have at most kRowSlots partial answers each (many
 // rows, few pieces per request: multi-token verification, large batches, DCP shards).
-// Two waves per output row, each lane owning 4 of the 512 columns; all of a row's partial
-// answers and LSEs are loaded in one round trip, the LSE maximum and the weights are
-// reduced across the wave's lanes, and each lane forms its columns' weighted sum.  Block
-// b serves rows 2b and 2b + 1 (one per pair of waves).
+// One wave per (output row, 256-column half), each lane owning 4 of the row's columns;
+// all of the row's partial answers and LSEs are loaded in one round trip, the LSE maximum
+// and the weights are reduced across the wave's lanes, and each lane forms its columns'
+// weighted sum.  Block b serves row b / 2, half b % 2.  One-wave workgroups spread the
+// loads over as many compute units as there are row halves (a compute unit takes in about
+// 55 GB/s): with 16 rows of 16 parts (tiny) four-wave workgroups left the merge waiting
+// 1.1 us on its loads.
 constexpr int kRowSlots = 32;
+constexpr int kRowMergeThreads = 64;
 
 template <bool PART_BF16, bool OUT_BF16, bool DECODE>
-__global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MLA_MERGE_LEAD_ARGS, MergeParams p,
-                                                                      int64_t total_rows) {
+__global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_MERGE_LEAD_ARGS, MergeParams p,
+                                                                         int64_t total_rows) {
   const int64_t a_rows = a_rows32, a_total = p.total_pages;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t orow = 2 * (int64_t)blockIdx.x + (wave >> 1);
-  const int col = (wave & 1) * 256 + lane * 4;
+  const int lane = threadIdx.x;
+  const int64_t orow = (int64_t)(blockIdx.x >> 1);  // < total_rows: the grid is 2 total_rows
+  const int col = (blockIdx.x & 1) * 256 + lane * 4;
   const int64_t grp = (int64_t)((uint32_t)orow / (uint32_t)a_rows);  // rows * groups < 2^31
   const int64_t row = orow - grp * a_rows;
-  // the block's two rows belong to request g0 or g0 + 1
-  const int64_t g0 = (int64_t)((uint32_t)(2 * blockIdx.x) / (uint32_t)a_rows);
   DevicePages dp{0, 0, 0, 0};
   if (DECODE && a_plan_n == 0 && a_mode == SPLIT_BALANCED) {  // uniform over the workgroup
-    __shared__ int64_t sm_xs[kMergeWaves][4];
-    dp = device_pages(p.seq_lens, p.batch, p.max_pages, g0, sm_xs);
+    int64_t unused[1][4];
+    dp = device_pages<1>(p.seq_lens, p.batch, p.max_pages, grp, unused);
   }
-  if (orow >= total_rows) return;  // the whole wave
+  const int64_t g0 = grp;
 
   int64_t s0 = 0, s1 = 0;
   bool inconsistent = false;
@@ -1619,7 +1624,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_rows_kernel(MLA_MERGE
     else
       *(f32x4*)((float*)p.out + off) = v;
   }
-  if (p.out_lse && (wave & 1) == 0 && lane == 0)
+  if (p.out_lse && (blockIdx.x & 1) == 0 && lane == 0)
     p.out_lse[orow] = inconsistent ? __builtin_nanf("") : (empty ? kNegInf : M + log2_fast(den) * kLn2);
 }
 
@@ -1818,10 +1823,10 @@ hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64
                         int max_row_slots, uint32_t lds_reserve, hipStream_t stream) {
   const int sel = (part_bf16 ? 4 : 0) + (p.out_bf16 ? 2 : 0) + (decode ? 1 : 0);
   if (max_row_slots <= kRowSlots) {
-    const dim3 grid((unsigned)((total_rows + 1) / 2));
+    const dim3 grid((unsigned)(2 * total_rows));
     switch (sel) {
 #define MLA_MERGE_CASE(S, A, B, D) \
-      case S: hipLaunchKernelGGL((mla_merge_rows_kernel<A, B, D>), grid, dim3(kMergeThreads), lds_reserve, stream, \
+      case S: hipLaunchKernelGGL((mla_merge_rows_kernel<A, B, D>), grid, dim3(kRowMergeThreads), lds_reserve, stream, \
                                  MLA_MERGE_LEAD_VALUES(p), p, total_rows); break;
       MLA_MERGE_CASE(0, false, false, false)
       MLA_MERGE_CASE(1, false, false, true)

@@ -802,7 +802,7 @@ LARGE_BATCH = [
     # batch, q_len, heads, kv, splits, lengths
     (300, 1, 16, "bf16", 0, "short"),       # one request per scan thread, row-wise merge
     (600, 1, 16, "bf16", 0, "tiny"),        # two requests per scan thread
-    (90, 1, 7, "bf16", 0, "short"),         # odd row count: merge blocks straddle requests
+    (90, 1, 7, "bf16", 0, "short"),         # odd row count per request
     (80, 1, 16, "bf16", 0, "one_long"),     # > 32 parts for one request: column-chunk merge
     (100, 2, 16, "fp8_e4m3fn", 0, "short"),
     (130, 1, 48, "bf16", 0, "short"),       # several row groups
@@ -815,7 +815,7 @@ def test_large_batch_device_lengths_full(case):
     """Past 64 requests every workgroup finds its pages and slots from the device lengths
     by a workgroup scan: every request of the batch matches the oracle, including the
     shortest requests the plan accepts, requests whose pages span several units and
-    requests split between the two rows of a merge block."""
+    head counts that are not a multiple of 16."""
     B, T, H, kv, splits, mix = case
     rng = np.random.default_rng(605 + B + H)
     lens = rng.integers(T, 130 if mix == "tiny" else 400, size=B)
