@@ -534,6 +534,19 @@ def test_hidden_tails_reproduce_causal_and_full(B, T, H, kv, f8qk):
     assert not np.array_equal(l_c, l_n)  # the two patterns do differ
 
 
+@pytest.mark.parametrize("splits", [0, 3])
+def test_hidden_tails_one_row_block(splits):
+    """One token and 12 heads (one row block): hidden tails on pieces of one page (auto
+    splits here) and of several pages equal the oracle over the histories shortened by the
+    tails."""
+    lens = np.array([700, 130, 64, 65, 1000], dtype=np.int32)
+    hid = np.array([[5], [64], [0], [1], [999]], dtype=np.int32)
+    wl = wk.make_workload(None, seed=310, batch=5, q_len=1, num_heads=12, seq_lens=list(lens))
+    o, l = run_gpu(wl, num_splits=splits, hidden=hid)
+    o_ref, l_ref = run_oracle(dataclasses_replace(wl, seq_lens=lens - hid[:, 0]))
+    compare(wl, o, l, o_ref, l_ref, f"hidden tails, one row block, splits={splits}")
+
+
 def test_hidden_tail_covering_the_history_gives_empty_rows():
     wl = wk.make_workload(None, seed=304, batch=2, q_len=2, num_heads=16, seq_lens=[300, 500])
     hidden = np.array([[0, 300], [-5, 499]], dtype=np.int32)  # (1, 1): everything hidden
@@ -689,12 +702,14 @@ def test_table_swap_is_caught():
     assert np.abs(o - o_bad).max() <= TOL_O["bf16"] and np.abs(l - l_bad).max() <= TOL_LSE
 
 
-def test_out_of_range_page_gives_nan_not_fault():
-    """A page id outside the pool is never dereferenced; that request's rows are NaN."""
+@pytest.mark.parametrize("splits", [2, 0])
+def test_out_of_range_page_gives_nan_not_fault(splits):
+    """A page id outside the pool is never dereferenced; that request's rows are NaN (auto
+    splits: pieces of one page)."""
     wl = wk.make_workload(None, seed=530, batch=3, q_len=1, num_heads=16, seq_lens=[300, 300, 300])
     bad = wl.block_table.copy()
     bad[1, 2] = wl.num_pages + 1000
-    o, l = run_gpu(wl, num_splits=2, block_table=bad)
+    o, l = run_gpu(wl, num_splits=splits, block_table=bad)
     assert np.isnan(l[1]).all() and np.isnan(o[1]).all()
     o_ref, l_ref = run_oracle(wl, requests=[0, 2])
     compare(wl, o[[0, 2]], l[[0, 2]], o_ref, l_ref, "other requests")
