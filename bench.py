@@ -52,7 +52,6 @@ RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312
 # (workload, splits, library version): a kernel change bumps the version, so `traffic`
 # reads null until the counters are taken again.
 _V071 = "mla_split_kv_decode_amd 0.7.1 (gfx950)"
-_V072 = "mla_split_kv_decode_amd 0.7.2 (gfx950)"  # 0.7.1's partial kernels; only the row-wise merge changed
 TRAFFIC = {
     ("long32k", 0, _V071): {"fetch_kib": 18600.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
     ("tiny", 0, _V071): {"fetch_kib": 738.5, "fetch_factor": 2.000, "write_kib": 520.0, "write_factor": 1.000},
@@ -61,7 +60,6 @@ TRAFFIC = {
                                 "write_factor": 1.000},
     ("dcp_fp8", 0, _V071): {"fetch_kib": 43571.1, "fetch_factor": 2.000, "write_kib": 15606.7, "write_factor": 1.000},
 }
-TRAFFIC.update({(w, s, _V072): v for (w, s, ver), v in list(TRAFFIC.items()) if ver == _V071})
 
 
 def traffic_of(name, splits, version):

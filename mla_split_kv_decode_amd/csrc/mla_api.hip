@@ -17,7 +17,7 @@
 
 namespace mla {
 hipError_t launch_partial(const PartialParams& p, bool fp8, bool fp8_qk, hipStream_t stream);
-bool partial_nt_parts(int64_t max_row_slots);
+bool partial_nt_parts(int64_t part_bytes, int64_t kv_bytes);
 hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64_t total_rows,
                         int max_row_slots, uint32_t lds_reserve, hipStream_t stream);
 constexpr long long kMaxLdsReserve = 128 * 1024;
@@ -142,7 +142,7 @@ mla_status scratch_of_current_device(void** out) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.7.2 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.7.3 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -450,8 +450,9 @@ mla_status decode_impl(const mla_plan* plan, const void* q, const mla_paged_kv* 
   pp.v_scale = fp8 ? kv->kv_scale : 1.0f;
   fill_plan_args(*plan, &pp.plan);
   pp.hidden = hidden;
-  pp.nt_parts = partial_nt_parts(plan->max_req_slots);
-  pp.stream_pages = plan->total_pages * (int64_t)mla_page_bytes(kPage, plan->kv_dtype) > kStreamKvBytes;
+  const int64_t kv_bytes = plan->total_pages * (int64_t)mla_page_bytes(kPage, plan->kv_dtype);
+  pp.nt_parts = partial_nt_parts((int64_t)plan->o_bytes, kv_bytes);
+  pp.stream_pages = kv_bytes > kStreamKvBytes;
   if (!out && !out_lse) {
     if (plan->num_wg > 0) {
       hipError_t e = launch_partial(pp, fp8, plan->fp8_qk != 0, st);

@@ -124,13 +124,20 @@ struct PartialParams {
   PlanArgs plan;
   const int32_t* hidden;  // null, or [B][T]: token t of request r does not see the last
                           // hidden[r][t] positions (replaces the causal pattern)
-  int32_t nt_parts;       // fp32 parts stored non-temporal (read by the column-chunk merge)
+  int32_t nt_parts;       // fp32 parts stored non-temporal (kNtPartBytes)
   int32_t stream_pages;   // one-row-block kernels: page copies with the non-temporal hint
 };
 
 // A layer's KV above this size is streamed past the caches (non-temporal page copies): the
 // memory-side cache (256 MB) could not keep the 24 layers' pools between decode steps.
 constexpr int64_t kStreamKvBytes = int64_t(8) << 20;
+
+// Partial answers go out with non-temporal stores when they are a large share of the
+// partial kernel's traffic: at least this many bytes and an eighth of the KV bytes (no
+// write-allocate in L2 and no dirty lines to write back when the kernel ends; long32k
+// and the 96-head DCP shard, 17-21%).  Smaller shares (ragged, verification, short
+// histories: under 2%, or under 1 MB) are left in the caches for the merge.
+constexpr int64_t kNtPartBytes = int64_t(4) << 20;
 
 // Launch parameters of the LSE merge kernel.
 enum MergeMode : int32_t { MERGE_GENERIC = 0, MERGE_DECODE = 1 };

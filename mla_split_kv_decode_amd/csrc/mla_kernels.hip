@@ -521,9 +521,10 @@ __device__ __forceinline__ void for_each_piece(const PartialParams& p, const Hot
 
 // Partial answer of one row of one piece to the workspace layout of mla_internal.h:
 // four consecutive columns starting at `col`.  NT: fp32 parts stored non-temporal, for
-// plans whose parts the column-chunk merge reads (more than kRowSlots a row): the
-// partial kernel ends sooner (long32k: 0.4 us of 11.6), while the row-wise merge, which
-// reads few parts a row, lost more on such parts than its partial kernel saved
+// plans whose parts are a large share of the kernel's traffic (kNtPartBytes): the partial
+// kernel ends sooner (long32k 0.4 us of 11.6; the 96-head DCP shard 2.4 us of 53, whose
+// 17 MB of parts otherwise sit dirty in L2 when the kernel ends), while plans with few
+// parts lost more in the merge than their partial kernel saved
 template <bool NT>
 __device__ __forceinline__ void store_partial(float* part_o, int64_t orow, int col, int nslots, int64_t slot,
                                               f32x4 v) {
@@ -1245,9 +1246,10 @@ __device__ __forceinline__ void partial_ks(
         for (int ct = 0; ct < CT; ct += 2) {
           const f32x4 a = acc[j][ct] * oscale, b = acc[j][ct + 1] * oscale;
           const f32x4 give = lo ? b : a;
-          f32x4 got;
+          f32x4 got;  // lane lrow ^ 8's: a DPP rotate by 8 within each 16-lane row
 #pragma unroll
-          for (int e = 0; e < 4; ++e) got[e] = __shfl_xor(give[e], 8);
+          for (int e = 0; e < 4; ++e)
+            got[e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give[e]), 0x128, 0xF, 0xF, false));
           const int c0 = 64 * wave + 16 * ct + 4 * lgrp;  // a's columns; b's are c0 + 16
           if (lo ? head_ok[j] : mate_ok)
             store_partial<true>(part_o, lo ? orow[j] : mate_row, lo ? c0 : c0 + 16, args.nslots, slot, lo ? a : got);
@@ -1769,11 +1771,10 @@ void launch_partial_k(const PartialParams& p, hipStream_t stream) {
 template <bool FP8, int RBW, bool F8QK = false>
 hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
   // hidden tails get kernels of their own (the per-piece table read costs the plain
-  // kernels a few percent when compiled in); non-temporal part stores only in the
-  // one-row-block kernel (the multi-row plans are merged row-wise)
-  const bool nt = RBW == 1 && p.nt_parts && !p.hidden;
+  // kernels a few percent when compiled in); non-temporal part stores as the plan says
+  const bool nt = p.nt_parts && !p.hidden;
   if (p.hidden) launch_partial_k<FP8, RBW, F8QK, true, false>(p, stream);
-  else if (nt) launch_partial_k<FP8, RBW, F8QK, false, RBW == 1>(p, stream);
+  else if (nt) launch_partial_k<FP8, RBW, F8QK, false, true>(p, stream);
   else launch_partial_k<FP8, RBW, F8QK, false, false>(p, stream);
   return hipGetLastError();
 }
@@ -1814,8 +1815,8 @@ hipError_t launch_kv_append(void* pool, int64_t num_pages, bool fp8, const int32
   return hipGetLastError();
 }
 
-bool partial_nt_parts(int64_t max_row_slots) {
-  return max_row_slots > kRowSlots;
+bool partial_nt_parts(int64_t part_bytes, int64_t kv_bytes) {
+  return part_bytes >= kNtPartBytes && 8 * part_bytes >= kv_bytes;
 }
 
 // lds_reserve: unused dynamic LDS per workgroup (the residency experiment), 0 normally.

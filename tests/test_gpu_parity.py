@@ -125,9 +125,13 @@ SMALL = [
     (2, 2, 96, [300, 100], 0, "bf16"),
     (2, 2, 96, [300, 100], 3, "fp8_e4m3fn"),
     (1, 4, 256, [130], 0, "bf16"),
-    # more than 32 parts a row: the column-chunk merge, fp32 parts stored non-temporal
+    # more than 32 parts a row: the column-chunk merge
     (1, 1, 16, [4000], 0, "fp8_e4m3fn"),
     (2, 1, 12, [4000, 2500], 0, "bf16"),
+    # parts of at least 4 MiB and an eighth of the KV: stored non-temporal (one row block
+    # FP8, column-chunk merge; two row blocks bf16, row-wise merge)
+    (1, 1, 16, [10000], 0, "fp8_e4m3fn"),
+    (1, 1, 96, [4000], 0, "bf16"),
 ]
 
 
