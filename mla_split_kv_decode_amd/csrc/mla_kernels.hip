@@ -43,6 +43,8 @@
 //             cross-lane reduction (row swaps) and an LDS exchange between the waves.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 
 // m0 is set inside the page-copy asm, the only user of m0 in these kernels
@@ -162,6 +164,28 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// x combined with op over the lanes lane ^ m for every power of two m in [LO, 64): DPP
+// moves inside each 16-lane row (quad permutes for 1 and 2; rotates by 4 and 8, which on
+// values already combined over the smaller offsets reach the same lanes as those xors),
+// then the gfx950 row swaps across rows.  All lanes active; every lane gets the result.
+template <int LO, class Op>
+__device__ __forceinline__ float wave_combine(float x, Op op) {
+  static_assert(LO == 1 || LO == 2 || LO == 4 || LO == 8 || LO == 16 || LO == 32, "offset");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  if constexpr (LO <= 1) x = op(x, dpp(x, std::integral_constant<int, 0xB1>{}));   // quad_perm 1,0,3,2
+  if constexpr (LO <= 2) x = op(x, dpp(x, std::integral_constant<int, 0x4E>{}));   // quad_perm 2,3,0,1
+  if constexpr (LO <= 4) x = op(x, dpp(x, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  if constexpr (LO <= 8) x = op(x, dpp(x, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  if constexpr (LO <= 16) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Eight FP8 E4M3FN codes (little-endian bytes of `raw`) -> eight bf16, exactly.
@@ -1285,8 +1309,10 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeWaves = kMergeThreads / 64;
 
 __device__ __forceinline__ float nan_max(float a, float b) {
-  // a NaN LSE (a piece that met a bad page id) must reach the output
-  return a != a ? a : (b != b ? b : fmaxf(a, b));
+  // a NaN LSE (a piece that met a bad page id) must reach the output (a select, not a
+  // branch: fmaxf alone would return the other operand)
+  const float m = fmaxf(a, b);
+  return (a == a && b == b) ? m : __builtin_nanf("");
 }
 
 template <bool PART_BF16>
@@ -1443,19 +1469,28 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
     else return s * a_rows + row;
   };
 
-  // first round: loads of O and LSE together
+  // first round: every pass's LSE, then every pass's O, all in flight together (loads
+  // complete in order, so the LSE maximum and its exchange need not wait for the O loads).
+  // Slots past the range load slot s0 (always a valid address) and are masked afterwards,
+  // so the loads carry no branches.
   float o[kPasses][kCPT];
   float l[kPasses];
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
     const int64_t s = s0 + sl + kSPP * k;
-    const bool ok = s < s1;
-    l[k] = ok ? lead_part_lse[lse_index(s)] : kNegInf;
-    if (ok) load_piece<PART_BF16>(lead_part_o, o_index(s), o[k]);
-    else {
+    l[k] = lead_part_lse[lse_index(s < s1 ? s : s0)];
+  }
 #pragma unroll
-      for (int c = 0; c < kCPT; ++c) o[k][c] = 0.f;
-    }
+  for (int k = 0; k < kPasses; ++k) {
+    const int64_t s = s0 + sl + kSPP * k;
+    load_piece<PART_BF16>(lead_part_o, o_index(s < s1 ? s : s0), o[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const bool ok = s0 + sl + kSPP * k < s1;
+    l[k] = ok ? l[k] : kNegInf;
+#pragma unroll
+    for (int c = 0; c < kCPT; ++c) o[k][c] = ok ? o[k][c] : 0.f;
   }
   // M over all slots (later rounds: LSEs only)
   float mx = kNegInf;
@@ -1463,8 +1498,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) mx = nan_max(mx, l[k]);
   for (int64_t s = s0 + 256 + tid; s < s1; s += kMergeThreads) mx = nan_max(mx, lead_part_lse[lse_index(s)]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = nan_max(mx, __shfl_xor(mx, off));
+  mx = wave_combine<1>(mx, [](float a, float b) { return nan_max(a, b); });
   if (lane == 0) sm_m[wave] = mx;
   __syncthreads();
   float M = sm_m[0];
@@ -1499,12 +1533,10 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
   }
   // sum over the slot lanes: lanes cp + kTPS k of a wave, then the waves.  Every thread of
   // a slot lane holds the same weights, so the denominator is summed over slot lanes only.
+  auto plus = [](float a, float b) { return a + b; };
 #pragma unroll
-  for (int off = kTPS; off < 64; off <<= 1) {
-#pragma unroll
-    for (int c = 0; c < kCPT; ++c) acc[c] += __shfl_xor(acc[c], off);
-    den += __shfl_xor(den, off);
-  }
+  for (int c = 0; c < kCPT; ++c) acc[c] = wave_combine<kTPS>(acc[c], plus);
+  den = wave_combine<kTPS>(den, plus);
   if (lane < kTPS) {
 #pragma unroll
     for (int c = 0; c < kCPT; ++c) sm_acc[wave][lane][c] = acc[c];
@@ -1588,9 +1620,10 @@ __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_ME
     if constexpr (DECODE) return ((row * kMergeChunks + (col >> 5)) * a_nslots + s) * kMergeCols + (col & 31);
     else return (s * a_rows + row) * kDV + col;
   };
-  // all loads of the row at once: lane k < ns holds LSE of slot s0 + k
-  const float l = lane < ns ? lead_part_lse[DECODE ? row * a_nslots + s0 + lane : (s0 + lane) * a_rows + row]
-                            : kNegInf;
+  // all loads of the row at once: lane k < ns holds LSE of slot s0 + k (lanes past ns load
+  // the range's first slot, a valid address, and are masked)
+  const int64_t ls = s0 + (lane < ns ? lane : 0);
+  const float lraw = lead_part_lse[DECODE ? row * a_nslots + ls : ls * a_rows + row];
   f32x4 o[kRowSlots];
 #pragma unroll
   for (int k = 0; k < kRowSlots; ++k) {
@@ -1604,13 +1637,10 @@ __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_ME
     }
   }
   inconsistent = inconsistent || dev_len != plan_len || ns > kRowSlots;
-  float M = l;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = nan_max(M, __shfl_xor(M, off));
+  const float l = lane < ns ? lraw : kNegInf;
+  const float M = wave_combine<1>(l, [](float x, float y) { return nan_max(x, y); });
   const float a = M == kNegInf ? 0.f : exp2_fast((l - M) * kLog2e);  // lanes past ns: 0
-  float den = a;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  const float den = wave_combine<1>(a, [](float x, float y) { return x + y; });
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < kRowSlots; ++k) {
