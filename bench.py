@@ -51,17 +51,15 @@ RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312
 # the copy-kernel calibration factors (profiles/<kernel>_<workload>.md), keyed by
 # (workload, splits, library version): a kernel change bumps the version, so `traffic`
 # reads null until the counters are taken again.
-_V073 = "mla_split_kv_decode_amd 0.7.3 (gfx950)"
-_V074 = "mla_split_kv_decode_amd 0.7.4 (gfx950)"  # 0.7.3's partial kernels; only the merges changed
+_V075 = "mla_split_kv_decode_amd 0.7.5 (gfx950)"
 TRAFFIC = {
-    ("long32k", 0, _V073): {"fetch_kib": 18597.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
-    ("tiny", 0, _V073): {"fetch_kib": 744.5, "fetch_factor": 2.000, "write_kib": 520.0, "write_factor": 1.000},
-    ("ragged", 0, _V073): {"fetch_kib": 566974.1, "fetch_factor": 2.000, "write_kib": 10314.6, "write_factor": 1.000},
-    ("spec_verify", 0, _V073): {"fetch_kib": 592344.8, "fetch_factor": 2.000, "write_kib": 16649.9,
+    ("long32k", 0, _V075): {"fetch_kib": 18597.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
+    ("tiny", 0, _V075): {"fetch_kib": 744.5, "fetch_factor": 2.000, "write_kib": 520.0, "write_factor": 1.000},
+    ("ragged", 0, _V075): {"fetch_kib": 566974.1, "fetch_factor": 2.000, "write_kib": 10314.9, "write_factor": 1.000},
+    ("spec_verify", 0, _V075): {"fetch_kib": 592341.1, "fetch_factor": 2.000, "write_kib": 16650.0,
                                 "write_factor": 1.000},
-    ("dcp_fp8", 0, _V073): {"fetch_kib": 43569.8, "fetch_factor": 2.000, "write_kib": 15600.0, "write_factor": 1.000},
+    ("dcp_fp8", 0, _V075): {"fetch_kib": 43569.2, "fetch_factor": 2.000, "write_kib": 15600.0, "write_factor": 1.000},
 }
-TRAFFIC.update({(w, sp, _V074): v for (w, sp, ver), v in list(TRAFFIC.items()) if ver == _V073})
 
 
 def traffic_of(name, splits, version):

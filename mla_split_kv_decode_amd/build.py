@@ -24,9 +24,10 @@ def hipcc():
     return "hipcc"
 
 
-def command(out=LIB, extra=()):
+def flags():
+    """Compiler flags of the library's sources (without inputs, outputs or -shared)."""
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed-fp32 VALU forms are kept out of the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # the kernels' leading arguments (what a workgroup needs before its first loads)
@@ -34,9 +35,20 @@ def command(out=LIB, extra=()):
         "-mllvm", "-amdgpu-kernarg-preload-count=14",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(REPO, "include"), "-I", CSRC,
-        *[os.path.join(CSRC, s) for s in SOURCES],
-        *extra, "-o", out,
     ]
+
+
+def command(out=LIB, extra=()):
+    return [hipcc(), *flags(), "-shared", *[os.path.join(CSRC, s) for s in SOURCES], *extra, "-o", out]
+
+
+def device_asm(source, out):
+    """Compile one source's device code to gfx950 assembly at `out` (for inspection)."""
+    cmd = [hipcc(), *flags(), "--cuda-device-only", "-S", os.path.join(CSRC, source), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    return out
 
 
 def build(verbose=False):

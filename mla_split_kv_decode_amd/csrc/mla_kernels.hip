@@ -97,6 +97,9 @@ __device__ __forceinline__ void barrier_lds() {
 // object at a constant offset): a run-time generic-to-LDS cast carries a null check on the
 // shared aperture, which the gfx950 code generator can emit as an illegal instruction.
 // Everything else takes integer LDS offsets from such a base.
+// The outputs are early-clobber ("=&v"): the reads of a call share one address register,
+// which must not double as the destination of an earlier read of the same call (a read
+// that returns before a later one issues would replace the address).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -108,12 +111,12 @@ __device__ __forceinline__ float lds_max_of(uint32_t off, float init) {
     asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:64\n\t"
                  "ds_read_b32 %2, %4 offset:128\n\tds_read_b32 %3, %4 offset:192\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]) : "v"(off));
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(off));
     return fmaxf(fmaxf(fmaxf(init, v[0]), fmaxf(v[1], v[2])), v[3]);
   } else {
     static_assert(G == 2, "exchange width");
     asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:64\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]) : "v"(off));
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(off));
     return fmaxf(fmaxf(init, v[0]), v[1]);
   }
 }
@@ -124,19 +127,19 @@ __device__ __forceinline__ float lds_sum_of(uint32_t off) {
     asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:64\n\t"
                  "ds_read_b32 %2, %4 offset:128\n\tds_read_b32 %3, %4 offset:192\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]) : "v"(off));
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(off));
     return ((v[0] + v[1]) + v[2]) + v[3];
   } else {
     static_assert(G == 2, "exchange width");
     asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:64\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]), "=v"(v[1]) : "v"(off));
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(off));
     return v[0] + v[1];
   }
 }
 // two 16-byte reads 1 KiB apart (the two 32-position P^T chunks of a row block)
 __device__ __forceinline__ void lds_read_pair_b128(uint32_t off, i32x4& a, i32x4& b) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(a), "=v"(b) : "v"(off));
+               : "=&v"(a), "=&v"(b) : "v"(off));
 }
 
 // A load of one int32 through the vector memory path.  Uniform loads would otherwise be
