@@ -87,11 +87,12 @@ typedef enum {
  *   block_table int32 [batch][max_pages_per_seq], physical page ids.  Only the first
  *               ceil(seq_lens[r]/page_size) entries of row r are read.
  *   seq_lens    int32 [batch], cached positions per request including its q_len query
- *               tokens.  Must equal the host copy the plan was made from: the merge
- *               stage compares them, and a request whose device length differs comes out
- *               as NaN rows (for batch <= 64 per request; above that, a total page count
- *               that differs makes every row NaN).  The partial stage works from the
- *               plan's copy (batch <= 64) and does not check.
+ *               tokens.  Must equal the host copy the plan was made from: for batch <= 64
+ *               the partial stage works from the plan's copy and compares each request's
+ *               device length with it, and a request that differs comes out as NaN rows
+ *               (its partial answers too); above 64 requests both stages read the device
+ *               lengths, and a total page count that differs from the plan's makes every
+ *               row NaN.
  */
 typedef struct {
   const void* pool;

@@ -86,8 +86,9 @@ MLA_HD int32_t fixed_page_begin(int32_t s, int32_t pages, int32_t S) {
 
 // The plan's host copy of the lengths, in the kernel arguments when the batch is small
 // enough, so that neither kernel waits for a device load of seq_lens before its first
-// real loads.  The device seq_lens are still read, in parallel, and a request whose
-// device length differs from the plan's gives NaN rows.
+// real loads.  The partial stage still reads the device seq_lens, under its page copies,
+// and a request whose device length differs from the plan's gives NaN pieces, which the
+// merge carries to the request's rows.
 constexpr int kArgBatch = 64;
 struct PlanArgs {
   int32_t n;                    // requests described here (0: derive from device seq_lens)

@@ -136,6 +136,20 @@ __device__ __forceinline__ float lds_sum_of(uint32_t off) {
     return v[0] + v[1];
   }
 }
+// lds_sum_of<4>(off), and the dword at off2 in the same round trip
+__device__ __forceinline__ float lds_sum4_and_b32(uint32_t off, uint32_t off2, int32_t& u) {
+  float v[4];
+  asm volatile("ds_read_b32 %0, %5\n\tds_read_b32 %1, %5 offset:64\n\t"
+               "ds_read_b32 %2, %5 offset:128\n\tds_read_b32 %3, %5 offset:192\n\t"
+               "ds_read_b32 %4, %6\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(u) : "v"(off), "v"(off2));
+  return ((v[0] + v[1]) + v[2]) + v[3];
+}
+// two consecutive dwords
+__device__ __forceinline__ void lds_read_pair_b32(uint32_t off, int32_t& a, int32_t& b) {
+  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:4\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b) : "v"(off));
+}
 // two 16-byte reads 1 KiB apart (the two 32-position P^T chunks of a row block)
 __device__ __forceinline__ void lds_read_pair_b128(uint32_t off, i32x4& a, i32x4& b) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
@@ -422,26 +436,36 @@ __device__ __forceinline__ void wait_pages(int n) {
   else wait_vmcnt<0>();
 }
 
-// The scalars of a partial-stage workgroup.  Those it needs before its first block-table
-// load (which pages, where the table and pool are, whose queries) arrive as the leading
-// kernel arguments, which the library is built to have preloaded into SGPRs with the
-// launch; the rest come from the parameter block, whose loads run meanwhile and are
-// settled (all of them at once, rather than one round trip per use inside a branch) once
-// the table loads are out.
+// The scalars of a partial-stage workgroup.  Everything a one-request plan needs before
+// its first page copy (which pages, where the table, pool and queries are, the row-block
+// shape, the pool's page count, the copy hint) arrives in the leading kernel arguments,
+// which the library is built to have preloaded into SGPRs with the launch (fourteen
+// dwords at most: small fields share a dword).  The rest come from the parameter block,
+// whose loads run meanwhile and are settled (all of them at once, rather than one round
+// trip per use inside a branch) once the first copies are out.
+//   unit_pack  = row groups | split mode << 16 | plan_n << 17
+//   shape_pack = heads | q_len << 16 | causal << 24 | stream << 25
+//   npages     = the pool's page count, saturated at 2^32 - 1 (page ids are int32)
 struct HotArgs {
-  int heads, hgroups, rgroups, mode, nwg, nsplits, plan_n, len0, maxp, batch, qlen, causal, nslots, stream;
-  int64_t total, npages;
+  int heads, hgroups, rgroups, mode, nwg, plan_n, len0, maxp, qlen, causal, stream;
+  uint32_t npages;
+  int64_t total32;  // the plan's page total (plan_n > 0)
+  // from the parameter block
+  int nsplits, batch, nslots;
+  int64_t total_dev;  // page total of the device lengths (plan_n = 0)
   float sscale, vscale;
-  __device__ __forceinline__ HotArgs(const PartialParams& p, int nwg_, int rgroups_, int mode_, int plan_n_,
-                                     int total32, int len0_, int maxp_, int heads_)
-      : heads(heads_), hgroups(p.head_groups), rgroups(rgroups_), mode(mode_), nwg(nwg_),
-        nsplits(p.num_splits), plan_n(plan_n_), len0(len0_), maxp(maxp_),
-        batch(p.batch), qlen(p.q_len), causal(p.causal), nslots(p.num_slots), stream(p.stream_pages),
-        total(plan_n_ > 0 ? (int64_t)total32 : p.total_pages), npages(p.num_pages), sscale(p.score_scale),
-        vscale(p.v_scale) {}
+  __device__ __forceinline__ HotArgs(const PartialParams& p, int nwg_, uint32_t unit_pack, int total32_, int len0_,
+                                     int maxp_, uint32_t shape_pack, uint32_t npages_)
+      : heads((int)(shape_pack & 0xFFFF)), hgroups((int)(((shape_pack & 0xFFFF) + kRowsPerBlock - 1) / kRowsPerBlock)),
+        rgroups((int)(unit_pack & 0xFFFF)), mode((int)((unit_pack >> 16) & 1)), nwg(nwg_),
+        plan_n((int)(unit_pack >> 17)), len0(len0_), maxp(maxp_), qlen((int)((shape_pack >> 16) & 0xFF)),
+        causal((int)((shape_pack >> 24) & 1)), stream((int)((shape_pack >> 25) & 1)), npages(npages_),
+        total32(total32_), nsplits(p.num_splits), batch(p.batch), nslots(p.num_slots),
+        total_dev(p.total_pages), sscale(p.score_scale), vscale(p.v_scale) {}
+  // a block-table entry outside the pool
+  __device__ __forceinline__ bool bad_id(int32_t id) const { return id < 0 || (uint32_t)id >= npages; }
   __device__ __forceinline__ void settle() const {
-    asm volatile("" ::"s"(hgroups), "s"(nsplits), "s"(batch), "s"(qlen), "s"(causal), "s"(nslots),
-                 "s"(stream), "s"(npages), "s"(sscale), "s"(vscale));
+    asm volatile("" ::"s"(nsplits), "s"(batch), "s"(nslots), "s"(total_dev), "s"(sscale), "s"(vscale));
   }
 };
 
@@ -518,10 +542,10 @@ __device__ __forceinline__ void for_each_piece(const PartialParams& p, const Hot
     const int pages = pages_of(L, a.maxp);
     run_piece(r, fixed_page_begin(sp, pages, S), fixed_page_begin(sp + 1, pages, S), w, L);
   } else if (a.plan_n == 1) {  // one request: its pages are the whole page axis
-    const int64_t gb = balanced_start(w, a.total, a.nwg), ge = balanced_start(w + 1, a.total, a.nwg);
+    const int64_t gb = balanced_start(w, a.total32, a.nwg), ge = balanced_start(w + 1, a.total32, a.nwg);
     run_piece(0, (int)gb, (int)ge, w, a.len0);
   } else if (use_plan) {
-    const int64_t P = a.total;
+    const int64_t P = a.total32;
     const int64_t gb = balanced_start(w, P, a.nwg), ge = balanced_start(w + 1, P, a.nwg);
     for (int r = 0; r < a.plan_n; ++r) {
       const int64_t pre = p.plan.pre[r], nxt = p.plan.pre[r + 1];
@@ -534,7 +558,7 @@ __device__ __forceinline__ void for_each_piece(const PartialParams& p, const Hot
   } else {
     int r;
     int64_t pre, gb, ge;
-    if (!device_unit_start<NW>(seq_lens, a.batch, a.maxp, w, a.nwg, a.total, xch, r, pre, gb, ge)) return;
+    if (!device_unit_start<NW>(seq_lens, a.batch, a.maxp, w, a.nwg, a.total_dev, xch, r, pre, gb, ge)) return;
     for (; r < a.batch && pre < ge; ++r) {
       const int L = max(seq_lens[r], 0);
       const int pr = pages_of(L, a.maxp);
@@ -607,6 +631,7 @@ struct KSplitSmem {
   __attribute__((aligned(16))) unsigned char pbuf[RBW][kPbufBytes];
   float red[RBW][4 * 16];                                             // row maxima of the sub-tiles
   float red2[RBW][4 * 16];                                            // row denominators (epilogue)
+  int32_t dlen[4];  // the piece's device length (plan path), landed by wave 0's LDS-DMA
 };
 
 // The (unit, row group) of this workgroup; false for a block past the last unit (the grid
@@ -682,6 +707,8 @@ __device__ __forceinline__ void partial_ks(
   const uint32_t red_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, red) - __builtin_offsetof(SM, tiles));
   const uint32_t red2_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, red2) - __builtin_offsetof(SM, tiles));
   const uint32_t pbuf_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, pbuf) - __builtin_offsetof(SM, tiles));
+  const uint32_t sx_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, sx) - __builtin_offsetof(SM, tiles));
+  const uint32_t dlen_lds = tiles_lds + (uint32_t)(__builtin_offsetof(SM, dlen) - __builtin_offsetof(SM, tiles));
 
   auto run_piece = [&](int r, int pb, int pe, int64_t slot, int L) {
     if constexpr (HID) {  // per-(request, token) hidden tails instead of the causal pattern
@@ -701,7 +728,7 @@ __device__ __forceinline__ void partial_ks(
     auto issue_id = [&](int i, int32_t id) {
       if (i >= n) return;
       const int lp = pb + i;
-      if ((uint64_t)(int64_t)id >= (uint64_t)args.npages) {
+      if (args.bad_id(id)) {
         bad = true;
         id = 0;
       }
@@ -720,7 +747,7 @@ __device__ __forceinline__ void partial_ks(
       pc_go = i < n;
       if (!pc_go) return;
       const int lp = pb + i;
-      if ((uint64_t)(int64_t)id >= (uint64_t)args.npages) {
+      if (args.bad_id(id)) {
         bad = true;
         id = 0;
       }
@@ -730,19 +757,45 @@ __device__ __forceinline__ void partial_ks(
     };
 
     // ---- queries through LDS (one HBM read per workgroup), then the first pages.  The
-    // one-row-block bf16 kernel (mostly two pages a piece) requests the block-table
-    // entries of its first pages before the query copies, so their round trip runs under
-    // them (unconditional loads from valid entries: the piece's last page for ti >= n,
-    // block_table[0] for an empty piece); the other kernels measured faster without.
+    // one-row-block bf16 kernel (mostly two pages a piece) fetches the block-table entries
+    // of its first pages ahead of the query copies, over LDS-DMA into this wave's slot of
+    // the k-half score buffer (untouched until the first page's scores, several barriers
+    // later): the wait for them is then explicit and covers nothing else, so the first
+    // page copy goes out one memory round trip after entry, while the parameter block's
+    // loads are still in flight (valid entries only: the piece's last page for ti >= n,
+    // block_table[0] for an empty piece).  The other kernels measured faster without.
     constexpr bool kEarlyId = !FP8 && RBW == 1;
-    int32_t first_id[kTiles];
-#pragma unroll
-    for (int ti = 0; ti < kTiles; ++ti)
-      first_id[ti] = kEarlyId ? *(n > 0 ? trow + pb + min(ti, n - 1) : block_table) : 0;
-    args.settle();
+    static_assert(!kEarlyId || kTiles == 2, "two early entries");
+    static_assert(sizeof(sm.sx) >= C::NW * 64, "block-table slots");
+    const uint32_t bt_lds = __builtin_amdgcn_readfirstlane(sx_lds + wave * 64);
+    int32_t first_id[kTiles] = {};
+    if constexpr (kEarlyId) {
+      if (lane < kTiles) {
+        const int off = n > 0 ? (pb + min(lane, n - 1)) * 4 : 0;
+        const int32_t* src = n > 0 ? trow : block_table;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     :: "s"(bt_lds), "v"(off), "s"(src) : "memory", "m0");
+      }
+    }
     unsigned char* stage = tiles + kEarlyTiles * TG::kPageBytes;
     typename C::QC(wave, lane)(tiles_lds + kEarlyTiles * TG::kPageBytes, q_ptr + (int64_t)r * args.qlen * args.heads * kDLatent, args.heads,
                                args.hgroups, g * RBW, rb_last);
+    if constexpr (kEarlyId) {
+      wait_vmcnt<C::QC::kPer>();  // the entries are older than the query copies
+      lds_read_pair_b32(bt_lds, first_id[0], first_id[1]);
+#pragma unroll
+      for (int ti = 0; ti < kTiles; ++ti) first_id[ti] = __builtin_amdgcn_readfirstlane(first_id[ti]);
+    }
+    // plan path: a request whose device length differs from the plan's gives a NaN piece
+    // (the merge carries a NaN LSE to the row).  Wave 0 fetches the length over LDS-DMA
+    // between the query copies and the first page copies, so the wait for the queries
+    // covers it and no compiler-counted load stays in flight through the page loop; it is
+    // compared in the epilogue.
+    if (args.plan_n > 0 && wave == 0 && lane == 0) {
+      const uint32_t dl = __builtin_amdgcn_readfirstlane(dlen_lds);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                   :: "s"(dl), "v"(r * 4), "s"(seq_lens) : "memory", "m0");
+    }
     int early = 0;
 #pragma unroll
     for (int ti = 0; ti < kEarlyTiles; ++ti) {
@@ -750,7 +803,8 @@ __device__ __forceinline__ void partial_ks(
       else issue(ti);
       early += ti < n ? 1 : 0;
     }
-    wait_pages<kPer, kEarlyTiles>(early);  // the query copies are older: all landed
+    args.settle();
+    wait_pages<kPer, kEarlyTiles>(early);  // the query copies (and the length) are older: all landed
     barrier_lds();
     i32x4 qf[NQ][KQ];  // this wave's queries: half of each row block's, or all of one
 #pragma unroll
@@ -906,7 +960,7 @@ __device__ __forceinline__ void partial_ks(
           int32_t id = k ? id1 : id0;
           cg[k] = ip < n;
           if (!cg[k]) continue;
-          if ((uint64_t)(int64_t)id >= (uint64_t)args.npages) {
+          if (args.bad_id(id)) {
             bad = true;
             id = 0;
           }
@@ -1249,13 +1303,21 @@ __device__ __forceinline__ void partial_ks(
       }
     }
     barrier_lds();
+    int dev_len = L;
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
-      const float ls = lds_sum_of<4>(red2_lds + 4 * (j * 64 + lrow));
+      float ls;
+      if (j == 0) {  // the device length comes with the first row block's denominators
+        int32_t dl;
+        ls = lds_sum4_and_b32(red2_lds + 4 * lrow, dlen_lds, dl);
+        if (args.plan_n > 0) dev_len = dl;
+      } else {
+        ls = lds_sum_of<4>(red2_lds + 4 * (j * 64 + lrow));
+      }
       const bool empty = m[j] == kNegInf;
       float oscale = empty ? 0.f : args.vscale / ls;
       float lse = empty ? kNegInf : (m[j] + log2_fast(ls)) * kLn2;
-      if (bad) {
+      if (bad || dev_len != L) {
         oscale = __builtin_nanf("");
         lse = __builtin_nanf("");
       }
@@ -1380,24 +1442,20 @@ __device__ __forceinline__ DevicePages device_pages(const int32_t* __restrict__ 
 }
 
 // Slot range [s0, s1) of request grp's partial answers.  Under SPLIT_BALANCED every work
-// unit owns at least one page (W <= P), so every slot in the range holds a piece.  On the
-// plan path the device length (a vector load, waited for only where it is compared, after
-// the partial answers have been loaded) must equal the plan's: the caller compares
-// dev_len with plan_len.  Device lengths under SPLIT_BALANCED come in `dp` (device_pages
-// with g0 = grp or grp - 1).
+// unit owns at least one page (W <= P), so every slot in the range holds a piece.  A
+// one-request plan needs only the preloaded arguments here, so its first loads go out at
+// entry; the plan path reads the plan's prefix page counts from the parameter block.  (A
+// device length that differs from the plan's is caught by the partial stage, whose
+// pieces of that request are NaN: every request of a plan has at least one piece.)
+// Device lengths under SPLIT_BALANCED come in `dp` (device_pages with g0 = grp or
+// grp - 1).
 __device__ __forceinline__ void decode_slots(const MergeParams& p, int64_t grp, int plan_n, int mode,
-                                             int nsplits, int nwg, int64_t total, int len0,
-                                             const DevicePages& dp, int64_t g0,
-                                             int64_t& s0, int64_t& s1, bool& inconsistent,
-                                             int& dev_len, int& plan_len) {
+                                             int nsplits, int nwg, const DevicePages& dp, int64_t g0,
+                                             int64_t& s0, int64_t& s1, bool& inconsistent) {
+  const int64_t total = p.total_pages;  // plan and device paths only
   if (plan_n == 1) {  // one request
-    dev_len = vector_load_i32(p.seq_lens);
-    plan_len = len0;
     s1 = mode == SPLIT_FIXED ? nsplits : nwg;
-  } else if (plan_n > 0) {
-    // slot range from the plan's lengths; the device length is only compared with it
-    dev_len = vector_load_i32(p.seq_lens + grp);
-    plan_len = p.plan.len[grp];
+  } else if (plan_n > 0) {  // slot range from the plan's lengths
     if (mode == SPLIT_FIXED) {
       s0 = grp * nsplits;
       s1 = s0 + nsplits;
@@ -1438,7 +1496,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
   __shared__ float sm_acc[kMergeWaves][kTPS][kCPT];
   __shared__ float sm_den[kMergeWaves];
   __shared__ int64_t sm_xs[kMergeWaves][4];
-  const int64_t a_rows = a_rows32, a_total = p.total_pages;
+  const int64_t a_rows = a_rows32;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1452,15 +1510,13 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
   // slot range [s0, s1) of this group
   int64_t s0 = 0, s1 = 0;
   bool inconsistent = false;
-  int dev_len = 0, plan_len = 0;
   DevicePages dp{0, 0, 0, 0};
   if constexpr (!DECODE) {
     s1 = a_nparts;
   } else {
     if (a_plan_n == 0 && a_mode == SPLIT_BALANCED)  // uniform over the workgroup
       dp = device_pages<kMergeWaves>(p.seq_lens, p.batch, p.max_pages, grp, sm_xs);
-    decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, dp, grp, s0, s1, inconsistent,
-                 dev_len, plan_len);
+    decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, dp, grp, s0, s1, inconsistent);
   }
   const int64_t col = (int64_t)chunk * kMergeCols + cp * kCPT;
   auto o_index = [&](int64_t s) -> int64_t {
@@ -1497,7 +1553,6 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
   }
   // M over all slots (later rounds: LSEs only)
   float mx = kNegInf;
-  inconsistent = inconsistent || dev_len != plan_len;
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) mx = nan_max(mx, l[k]);
   for (int64_t s = s0 + 256 + tid; s < s1; s += kMergeThreads) mx = nan_max(mx, lead_part_lse[lse_index(s)]);
@@ -1599,7 +1654,7 @@ constexpr int kRowMergeThreads = 64;
 template <bool PART_BF16, bool OUT_BF16, bool DECODE>
 __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_MERGE_LEAD_ARGS, MergeParams p,
                                                                          int64_t total_rows) {
-  const int64_t a_rows = a_rows32, a_total = p.total_pages;
+  const int64_t a_rows = a_rows32;
   const int lane = threadIdx.x;
   const int64_t orow = (int64_t)(blockIdx.x >> 1);  // < total_rows: the grid is 2 total_rows
   const int col = (blockIdx.x & 1) * 256 + lane * 4;
@@ -1614,10 +1669,8 @@ __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_ME
 
   int64_t s0 = 0, s1 = 0;
   bool inconsistent = false;
-  int dev_len = 0, plan_len = 0;
   if constexpr (!DECODE) s1 = a_nparts;
-  else decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, a_total, a_len0, dp, g0, s0, s1, inconsistent,
-                    dev_len, plan_len);
+  else decode_slots(p, grp, a_plan_n, a_mode, a_nsplits, a_nwg, dp, g0, s0, s1, inconsistent);
   const int ns = (int)(s1 - s0);
   auto o_index = [&](int64_t s) -> int64_t {
     if constexpr (DECODE) return ((row * kMergeChunks + (col >> 5)) * a_nslots + s) * kMergeCols + (col & 31);
@@ -1639,7 +1692,7 @@ __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_ME
       }
     }
   }
-  inconsistent = inconsistent || dev_len != plan_len || ns > kRowSlots;
+  inconsistent = inconsistent || ns > kRowSlots;
   const float l = lane < ns ? lraw : kNegInf;
   const float M = wave_combine<1>(l, [](float x, float y) { return nan_max(x, y); });
   const float a = M == kNegInf ? 0.f : exp2_fast((l - M) * kLog2e);  // lanes past ns: 0
@@ -1780,11 +1833,11 @@ template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
 __global__ __launch_bounds__(kPartialThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     const int32_t* __restrict__ block_table, const uint8_t* __restrict__ pool, const uint16_t* __restrict__ q_ptr,
-    int32_t nwg, int32_t rgroups, int32_t mode, int32_t plan_n, int32_t total32, int32_t len0, int32_t maxp,
-    int32_t heads, PartialParams p, const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
+    int32_t nwg, uint32_t unit_pack, int32_t total32, int32_t len0, int32_t maxp, uint32_t shape_pack,
+    uint32_t npages, PartialParams p, const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
   __shared__ KSplitSmem<FP8, RBW> sm;
-  const HotArgs args(p, nwg, rgroups, mode, plan_n, total32, len0, maxp, heads);
+  const HotArgs args(p, nwg, unit_pack, total32, len0, maxp, shape_pack, npages);
   partial_ks<FP8, RBW, RBW == 2, F8QK, HID, NT>(p, args, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
 
@@ -1795,14 +1848,20 @@ namespace {
 template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
 void launch_partial_k(const PartialParams& p, hipStream_t stream) {
   const int32_t total32 = p.plan.n > 0 ? (int32_t)p.total_pages : 0;  // the plan path has P < 2^31
+  const uint32_t unit_pack = (uint32_t)p.row_groups | (uint32_t)(p.mode & 1) << 16 | (uint32_t)p.plan.n << 17;
+  const uint32_t shape_pack = (uint32_t)p.num_heads | (uint32_t)p.q_len << 16 | (uint32_t)(p.causal & 1) << 24 |
+                              (uint32_t)(p.stream_pages & 1) << 25;
+  const uint32_t npages = p.num_pages > (int64_t)UINT32_MAX ? UINT32_MAX : (uint32_t)p.num_pages;
   hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, HID, NT>), dim3(partial_grid(p.num_wg, p.row_groups)),
-                     dim3(kPartialThreads), 0, stream, p.block_table, p.pool, p.q, p.num_wg, p.row_groups,
-                     p.mode, p.plan.n, total32, p.plan.len[0], p.max_pages, p.num_heads, p, p.seq_lens,
-                     p.part_o, p.part_lse);
+                     dim3(kPartialThreads), 0, stream, p.block_table, p.pool, p.q, p.num_wg, unit_pack, total32,
+                     p.plan.len[0], p.max_pages, shape_pack, npages, p, p.seq_lens, p.part_o, p.part_lse);
 }
 
 template <bool FP8, int RBW, bool F8QK = false>
 hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
+  // the packed leading arguments' fields (kMaxRowBlocks keeps q_len <= 64 and heads <= 1024)
+  if (p.num_heads > 0xFFFF || p.q_len > 0xFF || p.row_groups > 0xFFFF || p.plan.n > 0x7FFF)
+    return hipErrorInvalidValue;
   // hidden tails get kernels of their own (the per-piece table read costs the plain
   // kernels a few percent when compiled in); non-temporal part stores as the plan says
   const bool nt = p.nt_parts && !p.hidden;
