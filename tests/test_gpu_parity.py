@@ -707,12 +707,15 @@ def test_table_swap_is_caught():
 
 
 @pytest.mark.parametrize("splits", [2, 0])
-def test_out_of_range_page_gives_nan_not_fault(splits):
-    """A page id outside the pool is never dereferenced; that request's rows are NaN (auto
-    splits: pieces of one page)."""
+@pytest.mark.parametrize("which", ["past_pool", "negative", "int32_max"])
+def test_out_of_range_page_gives_nan_not_fault(splits, which):
+    """A page id outside the pool (past its end, negative, or the largest int32) is never
+    dereferenced; that request's rows are NaN.  The entry is a piece's first page (two
+    splits: pieces of two and three pages; auto splits: pieces of one page), whose id the
+    one-row-block kernel fetches ahead of its query copies."""
     wl = wk.make_workload(None, seed=530, batch=3, q_len=1, num_heads=16, seq_lens=[300, 300, 300])
     bad = wl.block_table.copy()
-    bad[1, 2] = wl.num_pages + 1000
+    bad[1, 2] = {"past_pool": wl.num_pages + 1000, "negative": -3, "int32_max": 2**31 - 1}[which]
     o, l = run_gpu(wl, num_splits=splits, block_table=bad)
     assert np.isnan(l[1]).all() and np.isnan(o[1]).all()
     o_ref, l_ref = run_oracle(wl, requests=[0, 2])
