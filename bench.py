@@ -99,6 +99,10 @@ def parse():
                     help="comma-separated byte counts: time the decode with each as unused LDS "
                          "per merge workgroup (same binary; the residency experiment), instead "
                          "of the default line")
+    ap.add_argument("--timeline", action="store_true",
+                    help="device timestamps of one layer-step from the stamping build "
+                         "(libmla_decode_timeline.so, include/mla_timeline.h), instead of the "
+                         "default line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -330,6 +334,81 @@ def read_ceiling(args, mb, wk, wl, nl):
     }), flush=True)
 
 
+TL_PARTIAL = {0: "entry", 1: "first page copies issued", 2: "queries read", 3: "page 0 landed",
+              4: "page 1 landed", 5: "epilogue denominators", 6: "partial answers issued",
+              7: "partial answers stored"}
+TL_MERGE = {0: "entry", 1: "LSE maximum known", 2: "partial answers consumed", 3: "end"}
+
+
+def timeline(args, mb, wk, wl, splits, nl, big):
+    """Device timestamps of a layer-step (include/mla_timeline.h): a graph of `nl`
+    layer-steps captured, the stamps cleared, the graph replayed back to back (at least 96
+    layer-steps); the stamps are then those of the last layer-step.  µs from the first partial workgroup's entry: the median over
+    workgroups and the latest, per slot; per XCD (block index mod 8) the median of page 1
+    landing and of the stores done."""
+    import ctypes
+
+    import torch
+
+    lib = mb.load(build_if_missing=False)
+    lib.mla_timeline_read.restype = ctypes.c_int
+    lib.mla_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_timeline_clear.restype = ctypes.c_int
+    lib.mla_timeline_clear.argtypes = []
+    st = setup(mb, wk, wl, splits, nl, args.fp8_qk, device_pools=big)
+    step = st["step"]
+    for i in range(max(args.warmup, nl)):
+        step(i % nl)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(nl):
+            step(i)
+    torch.cuda.synchronize()
+    if lib.mla_timeline_clear() != 0:  # no stamp of another launch shape survives
+        sys.exit("mla_timeline_clear failed")
+    for _ in range(max(3, 96 // nl)):  # back to back, so the last layer-step runs at working clocks
+        g.replay()
+    torch.cuda.synchronize()
+    part = np.zeros(4096 * 8, dtype=np.uint64)
+    merge = np.zeros(16384 * 4, dtype=np.uint64)
+    if lib.mla_timeline_read(part.ctypes.data, merge.ctypes.data) != 0:
+        sys.exit("mla_timeline_read failed")
+    part = part.reshape(4096, 8).astype(np.int64)
+    merge = merge.reshape(16384, 4).astype(np.int64)
+    blocks = np.nonzero(part[:, 0])[0]
+    t0 = part[blocks, 0].min()
+
+    def table(stamps, rows, names):
+        out = {}
+        for k, name in names.items():
+            v = stamps[rows, k]
+            v = v[v > 0]
+            if len(v):
+                us = (v - t0) * 0.01  # 100 MHz clock
+                out[name] = {"median_us": round(float(np.median(us)), 2), "max_us": round(float(us.max()), 2)}
+        return out
+
+    mrows = np.nonzero(merge[:, 0])[0]
+    per_xcd = {}
+    for x in range(8):
+        sel = blocks[blocks % 8 == x]
+        per_xcd[str(x)] = {name: round(float(np.median((part[sel, k][part[sel, k] > 0] - t0) * 0.01)), 2)
+                           for k, name in ((4, "page 1 landed"), (7, "partial answers stored"))
+                           if (part[sel, k] > 0).any()}
+    print(json.dumps({
+        "metric": "device timeline of one layer-step (µs from the first partial workgroup's entry)",
+        "unit": "us", "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": describe(wl, splits), "layers_rotated": nl},
+        "library": mb.version() + " (timeline build)",
+        "partial_workgroups": int(len(blocks)), "merge_workgroups": int(len(mrows)),
+        "partial": table(part, blocks, TL_PARTIAL), "merge": table(merge, mrows, TL_MERGE),
+        "per_xcd": per_xcd,
+    }), flush=True)
+    del g, st
+    torch.cuda.synchronize()
+
+
 # Static LDS of the merge kernels (largest variant, from the kernel metadata), the LDS of
 # one compute unit and the allocation granule.
 MERGE_STATIC_LDS = 672
@@ -419,6 +498,10 @@ def main():
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
         return
+    if args.timeline:  # the same kernels with the stamps compiled in
+        from mla_split_kv_decode_amd import build as mbuild
+
+        mb.LIB_PATH = mbuild.LIB_TIMELINE
     mb.load(build_if_missing=False)
     torch.cuda.set_device(0)
     over = {}
@@ -438,6 +521,9 @@ def main():
 
     if args.read_ceiling:
         read_ceiling(args, mb, wk, wl, nl)
+        return
+    if args.timeline:
+        timeline(args, mb, wk, wl, splits, nl, big)
         return
     if args.lds_reserve:
         lds_residency(args, mb, wk, wl, splits, nl, big)

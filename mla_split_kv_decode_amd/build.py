@@ -13,6 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 REPO = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_decode.so")
+# the same sources with the timeline stamps compiled in (bench.py --timeline only)
+LIB_TIMELINE = os.path.join(PKG, "libmla_decode_timeline.so")
 SOURCES = ["mla_kernels.hip", "mla_api.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
@@ -51,10 +53,9 @@ def device_asm(source, out):
     return out
 
 
-def build(verbose=False):
-    """Compile the library (always, even when one is already built)."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _compile(out, extra, verbose):
+    tmp = out + ".tmp"
+    cmd = command(tmp, extra)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,9 +65,21 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False):
+    """Compile the library (always, even when one is already built)."""
+    return _compile(LIB, (), verbose)
+
+
+def build_timeline(verbose=False):
+    """Compile the timeline variant (include/mla_timeline.h): the same kernels, stamping."""
+    return _compile(LIB_TIMELINE, ("-DMLA_TIMELINE=1",), verbose)
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--timeline" in sys.argv:
+        print(build_timeline(verbose="-v" in sys.argv))

@@ -52,6 +52,35 @@
 
 namespace mla {
 
+// Timeline builds (-DMLA_TIMELINE=1, libmla_decode_timeline.so, read by bench.py --timeline):
+// wave 0 of each workgroup stamps the device's 100 MHz real-time clock at fixed points of
+// the decode (mla_timeline.h names them); the stamps of a workgroup's last piece are kept.
+// The stamp waits for the wave's outstanding scalar loads, so the entry stamp comes first
+// and no stamp sits between entry and the first copies of a piece.  In ordinary builds the
+// macros are empty.
+#ifdef MLA_TIMELINE
+constexpr int kTlBlocks = 4096, kTlSlots = 8, kTlMergeBlocks = 16384, kTlMergeSlots = 4;
+__device__ unsigned long long g_tl_partial[kTlBlocks * kTlSlots];
+__device__ unsigned long long g_tl_merge[kTlMergeBlocks * kTlMergeSlots];
+#define MLA_TL(k)                                                                              \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && blockIdx.x < kTlBlocks)                                            \
+      g_tl_partial[blockIdx.x * kTlSlots + (k)] = __builtin_amdgcn_s_memrealtime();            \
+  } while (0)
+#define MLA_TL_MERGE(k)                                                                        \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && blockIdx.x < kTlMergeBlocks)                                       \
+      g_tl_merge[blockIdx.x * kTlMergeSlots + (k)] = __builtin_amdgcn_s_memrealtime();         \
+  } while (0)
+#else
+#define MLA_TL(k) \
+  do {            \
+  } while (0)
+#define MLA_TL_MERGE(k) \
+  do {                  \
+  } while (0)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -146,9 +175,11 @@ __device__ __forceinline__ float lds_sum4_and_b32(uint32_t off, uint32_t off2, i
   return ((v[0] + v[1]) + v[2]) + v[3];
 }
 // two consecutive dwords
-__device__ __forceinline__ void lds_read_pair_b32(uint32_t off, int32_t& a, int32_t& b) {
+template <int K>
+__device__ __forceinline__ void lds_read_ids(uint32_t off, int32_t (&v)[K]) {
+  static_assert(K == 2, "id count");
   asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:4\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(a), "=&v"(b) : "v"(off));
+               : "=&v"(v[0]), "=&v"(v[1]) : "v"(off));
 }
 // two 16-byte reads 1 KiB apart (the two 32-position P^T chunks of a row block)
 __device__ __forceinline__ void lds_read_pair_b128(uint32_t off, i32x4& a, i32x4& b) {
@@ -763,7 +794,9 @@ __device__ __forceinline__ void partial_ks(
     // later): the wait for them is then explicit and covers nothing else, so the first
     // page copy goes out one memory round trip after entry, while the parameter block's
     // loads are still in flight (valid entries only: the piece's last page for ti >= n,
-    // block_table[0] for an empty piece).  The other kernels measured faster without.
+    // block_table[0] for an empty piece).  The FP8 and two-row-block kernels, whose first
+    // pages wait for the queries anyway, measured faster with one scalar load per page
+    // (the same fetch: dcp_fp8 +0.7 us, spec_verify +1.0 us a layer-step).
     constexpr bool kEarlyId = !FP8 && RBW == 1;
     static_assert(!kEarlyId || kTiles == 2, "two early entries");
     static_assert(sizeof(sm.sx) >= C::NW * 64, "block-table slots");
@@ -782,7 +815,7 @@ __device__ __forceinline__ void partial_ks(
                                args.hgroups, g * RBW, rb_last);
     if constexpr (kEarlyId) {
       wait_vmcnt<C::QC::kPer>();  // the entries are older than the query copies
-      lds_read_pair_b32(bt_lds, first_id[0], first_id[1]);
+      lds_read_ids<kTiles>(bt_lds, first_id);
 #pragma unroll
       for (int ti = 0; ti < kTiles; ++ti) first_id[ti] = __builtin_amdgcn_readfirstlane(first_id[ti]);
     }
@@ -803,6 +836,7 @@ __device__ __forceinline__ void partial_ks(
       else issue(ti);
       early += ti < n ? 1 : 0;
     }
+    MLA_TL(1);  // the first page copies are out
     args.settle();
     wait_pages<kPer, kEarlyTiles>(early);  // the query copies (and the length) are older: all landed
     barrier_lds();
@@ -819,6 +853,7 @@ __device__ __forceinline__ void partial_ks(
       }
     }
     barrier_lds();  // the staging tiles are free again
+    MLA_TL(2);
 #pragma unroll
     for (int ti = kEarlyTiles; ti < kTiles; ++ti) {
       if constexpr (kEarlyId) issue_id(ti, first_id[ti]);
@@ -978,6 +1013,7 @@ __device__ __forceinline__ void partial_ks(
         if (i == 0) wait_pages<kPer, 2>(min(n, kTiles) - 2);
         else wait_vmcnt<0>();
         barrier_lds();  // pages i, i + 1 landed; every wave is done with pages i - 2, i - 1
+        if (i < 4) MLA_TL(3 + i / 2);
         cg[0] = cg[1] = false;
         if (i > 0) record_pair(i + 2, __builtin_amdgcn_readfirstlane(nid0), __builtin_amdgcn_readfirstlane(nid1));
         if (cg[0]) copy.template part<0, kA1>(cb[0], cs[0], cv[0]);
@@ -1065,6 +1101,7 @@ __device__ __forceinline__ void partial_ks(
         else
           wait_pages<kPer, kTiles - 1>(min(n, i + kTiles) - (i + 1));
         barrier_lds();  // every wave's copies of page i have landed
+        if (i < 2) MLA_TL(3 + i);
         if constexpr (kTopIssue) {
           pc_go = false;
           if (i > 0) record_copy(i + kTiles - 1, __builtin_amdgcn_readfirstlane(next_id));  // uniform
@@ -1303,6 +1340,7 @@ __device__ __forceinline__ void partial_ks(
       }
     }
     barrier_lds();
+    MLA_TL(5);
     int dev_len = L;
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
@@ -1354,6 +1392,11 @@ __device__ __forceinline__ void partial_ks(
         if (wave == 0 && lgrp == 0) part_lse[(int64_t)orow[j] * args.nslots + slot] = lse;
       }
     }
+#ifdef MLA_TIMELINE
+    MLA_TL(6);
+    wait_vmcnt<0>();
+    MLA_TL(7);
+#endif
     barrier_lds();  // tiles and exchange buffers are reused by the next piece
   };
 
@@ -1491,6 +1534,7 @@ __device__ __forceinline__ void decode_slots(const MergeParams& p, int64_t grp, 
 template <bool PART_BF16, bool OUT_BF16, bool DECODE>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD_ARGS, MergeParams p) {
   using MG = MergeGeom<PART_BF16>;
+  MLA_TL_MERGE(0);
   constexpr int kCPT = MG::kCPT, kTPS = MG::kTPS, kSPP = MG::kSPP, kPasses = MG::kPasses;
   __shared__ float sm_m[kMergeWaves];
   __shared__ float sm_acc[kMergeWaves][kTPS][kCPT];
@@ -1559,6 +1603,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
   mx = wave_combine<1>(mx, [](float a, float b) { return nan_max(a, b); });
   if (lane == 0) sm_m[wave] = mx;
   __syncthreads();
+  MLA_TL_MERGE(1);
   float M = sm_m[0];
 #pragma unroll
   for (int wv = 1; wv < kMergeWaves; ++wv) M = nan_max(M, sm_m[wv]);
@@ -1589,6 +1634,10 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
       }
     }
   }
+#ifdef MLA_TIMELINE
+  asm volatile("" ::"v"(acc[0]), "v"(acc[kCPT - 1]), "v"(den));
+  MLA_TL_MERGE(2);
+#endif
   // sum over the slot lanes: lanes cp + kTPS k of a wave, then the waves.  Every thread of
   // a slot lane holds the same weights, so the denominator is summed over slot lanes only.
   auto plus = [](float a, float b) { return a + b; };
@@ -1637,6 +1686,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MLA_MERGE_LEAD
           inconsistent ? __builtin_nanf("") : (empty ? kNegInf : M + log2_fast(d) * kLn2);
     }
   }
+  MLA_TL_MERGE(3);
 }
 
 // Row-wise merge, for plans whose rows have at most kRowSlots partial answers each (many
@@ -1654,6 +1704,7 @@ constexpr int kRowMergeThreads = 64;
 template <bool PART_BF16, bool OUT_BF16, bool DECODE>
 __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_MERGE_LEAD_ARGS, MergeParams p,
                                                                          int64_t total_rows) {
+  MLA_TL_MERGE(0);
   const int64_t a_rows = a_rows32;
   const int lane = threadIdx.x;
   const int64_t orow = (int64_t)(blockIdx.x >> 1);  // < total_rows: the grid is 2 total_rows
@@ -1695,6 +1746,7 @@ __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_ME
   inconsistent = inconsistent || ns > kRowSlots;
   const float l = lane < ns ? lraw : kNegInf;
   const float M = wave_combine<1>(l, [](float x, float y) { return nan_max(x, y); });
+  MLA_TL_MERGE(1);
   const float a = M == kNegInf ? 0.f : exp2_fast((l - M) * kLog2e);  // lanes past ns: 0
   const float den = wave_combine<1>(a, [](float x, float y) { return x + y; });
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1714,6 +1766,7 @@ __global__ __launch_bounds__(kRowMergeThreads) void mla_merge_rows_kernel(MLA_ME
   }
   if (p.out_lse && (blockIdx.x & 1) == 0 && lane == 0)
     p.out_lse[orow] = inconsistent ? __builtin_nanf("") : (empty ? kNegInf : M + log2_fast(den) * kLn2);
+  MLA_TL_MERGE(3);
 }
 
 // ------------------------------------------------------------------- cache append
@@ -1837,6 +1890,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     uint32_t npages, PartialParams p, const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
   __shared__ KSplitSmem<FP8, RBW> sm;
+  MLA_TL(0);
   const HotArgs args(p, nwg, unit_pack, total32, len0, maxp, shape_pack, npages);
   partial_ks<FP8, RBW, RBW == 2, F8QK, HID, NT>(p, args, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
 }
@@ -1952,3 +2006,21 @@ hipError_t launch_merge(const MergeParams& p, bool part_bf16, bool decode, int64
 }
 
 }  // namespace mla
+
+#ifdef MLA_TIMELINE
+// The stamps of the last decode, host copies: partial [4096][8], merge [16384][4] (uint64,
+// zero where a workgroup did not stamp).  0 on success.
+extern "C" int mla_timeline_read(unsigned long long* partial, unsigned long long* merge) {
+  if (hipMemcpyFromSymbol(partial, HIP_SYMBOL(mla::g_tl_partial), sizeof(mla::g_tl_partial)) != hipSuccess)
+    return 1;
+  if (hipMemcpyFromSymbol(merge, HIP_SYMBOL(mla::g_tl_merge), sizeof(mla::g_tl_merge)) != hipSuccess) return 2;
+  return 0;
+}
+extern "C" int mla_timeline_clear(void) {
+  static const unsigned long long zeros[mla::kTlMergeBlocks * mla::kTlMergeSlots] = {};
+  static_assert(sizeof(zeros) >= sizeof(mla::g_tl_partial), "clear source");
+  if (hipMemcpyToSymbol(HIP_SYMBOL(mla::g_tl_partial), zeros, sizeof(mla::g_tl_partial)) != hipSuccess) return 1;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(mla::g_tl_merge), zeros, sizeof(mla::g_tl_merge)) != hipSuccess) return 2;
+  return 0;
+}
+#endif

@@ -37,6 +37,24 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_timeline_build_exports_its_header(lib):
+    """The stamping variant (include/mla_timeline.h) exports what its header declares, on
+    top of the library's own symbols; the ordinary library exports none of it."""
+    from mla_split_kv_decode_amd import build as mbuild
+
+    tl_header = os.path.join(os.path.dirname(HEADER), "mla_timeline.h")
+    text = re.sub(r"/\*.*?\*/", "", open(tl_header).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["mla_timeline_clear", "mla_timeline_read"]
+    for n in names:
+        assert not hasattr(lib, n), n
+    if not os.path.exists(mbuild.LIB_TIMELINE):
+        pytest.skip("timeline build not present (build() makes it)")
+    tl = ctypes.CDLL(mbuild.LIB_TIMELINE)
+    for n in names + declared_functions():
+        assert hasattr(tl, n), n
+
+
 def test_version_and_status_strings(lib):
     assert "gfx950" in mb.version()
     assert mb.status_str(mb.MLA_OK) == "ok"
