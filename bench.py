@@ -51,14 +51,14 @@ RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312
 # the copy-kernel calibration factors (profiles/<kernel>_<workload>.md), keyed by
 # (workload, splits, library version): a kernel change bumps the version, so `traffic`
 # reads null until the counters are taken again.
-_V076 = "mla_split_kv_decode_amd 0.7.6 (gfx950)"
+_V077 = "mla_split_kv_decode_amd 0.7.7 (gfx950)"
 TRAFFIC = {
-    ("long32k", 0, _V076): {"fetch_kib": 18596.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
-    ("tiny", 0, _V076): {"fetch_kib": 742.0, "fetch_factor": 2.000, "write_kib": 520.0, "write_factor": 1.000},
-    ("ragged", 0, _V076): {"fetch_kib": 566958.1, "fetch_factor": 2.000, "write_kib": 10314.4, "write_factor": 1.000},
-    ("spec_verify", 0, _V076): {"fetch_kib": 592344.4, "fetch_factor": 2.000, "write_kib": 16650.0,
+    ("long32k", 0, _V077): {"fetch_kib": 18596.0, "fetch_factor": 2.000, "write_kib": 6240.0, "write_factor": 1.000},
+    ("tiny", 0, _V077): {"fetch_kib": 742.0, "fetch_factor": 2.000, "write_kib": 520.0, "write_factor": 1.000},
+    ("ragged", 0, _V077): {"fetch_kib": 566958.8, "fetch_factor": 2.000, "write_kib": 10314.4, "write_factor": 1.000},
+    ("spec_verify", 0, _V077): {"fetch_kib": 592344.8, "fetch_factor": 2.000, "write_kib": 16650.2,
                                 "write_factor": 1.000},
-    ("dcp_fp8", 0, _V076): {"fetch_kib": 43588.8, "fetch_factor": 2.000, "write_kib": 15600.0, "write_factor": 1.000},
+    ("dcp_fp8", 0, _V077): {"fetch_kib": 43588.8, "fetch_factor": 2.000, "write_kib": 15600.0, "write_factor": 1.000},
 }
 
 
