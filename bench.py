@@ -302,15 +302,16 @@ def wk_flops(wl):
     return wk.attention_flops(wl.seq_lens, wl.q_len, wl.num_heads, wl.causal)
 
 
-def read_ceiling(args, mb, wk, wl, nl):
+def read_ceiling(args, mb, wk, wl, nl, big=False):
     """A plain read of the workload's rotated pools: every byte once, into registers or
     into LDS as the partial stage copies them, one launch per pool; and an empty launch.
     The floor of any single launch per layer-step that streams the same bytes."""
     import torch
 
-    st = setup(mb, wk, wl, 0, nl)
-    kv_b = wk.kv_bytes(wl.seq_lens, wl.kv_format)
-    # exactly the KV bytes of each pool (its first pages; the pool's spare pages are left out)
+    st = setup(mb, wk, wl, 0, nl, device_pools=big)
+    # the KV bytes of each pool (its first pages; the pool's spare pages are left out),
+    # rounded down to whole KiB as the read kernels take them
+    kv_b = wk.kv_bytes(wl.seq_lens, wl.kv_format) // 1024 * 1024
     pools = [p.view(torch.uint8).view(-1)[:kv_b] for p, _ in st["pools"]]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     pool_b = kv_b
@@ -520,7 +521,7 @@ def main():
     splits = 0 if args.splits == "auto" else int(args.splits)
 
     if args.read_ceiling:
-        read_ceiling(args, mb, wk, wl, nl)
+        read_ceiling(args, mb, wk, wl, nl, big)
         return
     if args.timeline:
         timeline(args, mb, wk, wl, splits, nl, big)
