@@ -309,6 +309,38 @@ def test_random_shapes(case):
     compare(wl, o, l, o_ref, l_ref, f"B{B} T{T} H{H} s{splits} causal={causal} fp8qk={f8qk}")
 
 
+def _wide_cases(n, seed=777):
+    """A wider seeded draw: up to eight query tokens, 1 to 128 heads (odd head counts
+    and head groups included), up to six requests, fixed splits beyond a request's page
+    count, fp32 outputs on about a quarter of the cases."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kv = ["bf16", "fp8_e4m3fn"][rng.integers(2)]
+        T = int(rng.choice([1, 1, 2, 3, 4, 5, 6, 8]))
+        H = int(rng.choice([1, 5, 12, 16, 17, 32, 48, 64, 96, 128]))
+        while T * -(-H // 16) > 64:
+            H //= 2
+        B = int(rng.integers(1, 7))
+        seq = [int(rng.integers(T, 3000)) for _ in range(B)]
+        splits = int(rng.choice([0, 0, 0, 1, 2, 5, 16, 40]))
+        causal = bool(rng.integers(2))
+        f8qk = kv == "fp8_e4m3fn" and T * -(-H // 16) >= 2 and bool(rng.integers(3) == 0)
+        out_dtype = "fp32" if rng.integers(4) == 0 else "bf16"
+        cases.append((i, B, T, H, seq, splits, kv, causal, f8qk, out_dtype))
+    return cases
+
+
+@pytest.mark.parametrize("case", _wide_cases(120), ids=lambda c: f"w{c[0]}")
+def test_random_shapes_wide(case):
+    i, B, T, H, seq, splits, kv, causal, f8qk, out_dtype = case
+    wl = wk.make_workload(None, seed=50777 + i, batch=B, q_len=T, num_heads=H, seq_lens=seq,
+                          kv_format=kv, shuffled=True, num_splits=splits, causal=causal)
+    o, l = run_gpu(wl, canary=True, fp8_qk=f8qk, out_dtype=out_dtype)
+    o_ref, l_ref = run_oracle(wl)
+    compare(wl, o, l, o_ref, l_ref, f"B{B} T{T} H{H} s{splits} causal={causal} fp8qk={f8qk} out={out_dtype}")
+
+
 def test_spec_verify_full():
     """All 8 requests, 4 causal draft tokens each, 16 heads, 131,076 positions, at the
     16 partitions of the pages' policy and at auto splits."""
