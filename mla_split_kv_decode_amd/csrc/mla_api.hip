@@ -142,7 +142,7 @@ mla_status scratch_of_current_device(void** out) {
 
 extern "C" {
 
-const char* mla_version(void) { return "mla_split_kv_decode_amd 0.7.7 (gfx950)"; }
+const char* mla_version(void) { return "mla_split_kv_decode_amd 0.7.8 (gfx950)"; }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }
 

@@ -126,7 +126,7 @@ struct PartialParams {
   const int32_t* hidden;  // null, or [B][T]: token t of request r does not see the last
                           // hidden[r][t] positions (replaces the causal pattern)
   int32_t nt_parts;       // fp32 parts stored non-temporal (kNtPartBytes)
-  int32_t stream_pages;   // one-row-block kernels: page copies with the non-temporal hint
+  int32_t stream_pages;   // one-row-group kernels: page copies with the non-temporal hint
 };
 
 // A layer's KV above this size is streamed past the caches (non-temporal page copies): the

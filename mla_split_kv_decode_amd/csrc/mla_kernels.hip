@@ -390,14 +390,15 @@ struct OperandAddr {
 // `valid_rows` (the unwritten tail of a request's last page) are filled from the last
 // valid row instead: their scores are masked, so only their finiteness matters (a zero
 // softmax weight times a NaN left in the pool would still be NaN).
-// STREAM (one-row-block kernels, decided per launch): the copies carry the non-temporal
-// hint.  A page that one workgroup alone reads is then not kept in the caches, so the
-// small data every launch reuses (block table, queries, partial answers) stays resident:
-// long32k 15.93 -> 15.45 us a layer-step, ragged 217 -> 194 us (same-box A/B).  The plan
-// asks for it only when a layer's KV is too large for the memory-side cache to keep the
-// layers' pools between steps (tiny's 24 layers of 1.2 MB stay resident without the hint,
-// 5.70 against 5.96 us); pages that several row groups read from their XCD's L2 keep the
-// default policy (the hint cost dcp_fp8 and spec_verify 3% each).
+// STREAM (kernels of one-row-group plans): the copies carry the non-temporal hint.  A page
+// that one workgroup alone reads is then not kept in the caches, so the small data every
+// launch reuses (block table, queries, partial answers) stays resident: long32k 15.93 ->
+// 15.45 us a layer-step, ragged 217 -> 194 us, two draft tokens over 131K positions
+// (two row blocks) 212 -> 188 us (same-box A/B).  The plan asks for it only when a layer's
+// KV is too large for the memory-side cache to keep the layers' pools between steps
+// (tiny's 24 layers of 1.2 MB stay resident without the hint, 5.70 against 5.96 us);
+// pages that several row groups read from their XCD's L2 keep the default policy (the
+// hint cost dcp_fp8 and spec_verify 3% each).
 template <bool FP8, int NW, bool STREAM = false>
 struct PageCopy {
   using TG = TileGeom<FP8>;
@@ -701,7 +702,7 @@ __device__ __forceinline__ bool unit_of_block(int nwg, int rgroups, int64_t& w, 
   return w < nwg;
 }
 
-template <bool FP8, int RBW, bool RS, bool F8QK, bool HID, bool NT>
+template <bool FP8, int RBW, bool RS, bool F8QK, bool HID, bool NT, bool ST>
 __device__ __forceinline__ void partial_ks(
     const PartialParams& p, const HotArgs& args, const uint16_t* __restrict__ q_ptr,
     const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
@@ -750,8 +751,10 @@ __device__ __forceinline__ void partial_ks(
   int lag_max = 0;
 #pragma unroll
   for (int j = 0; j < RBW; ++j) lag_max = max(lag_max, lag[j]);
-  // one row block: this workgroup alone reads its pages (non-temporal copies)
-  const PageCopy<FP8, C::NW, RBW == 1> copy(wave, lane, args.stream);
+  // one row group: this workgroup alone reads its pages, so they may be copied with the
+  // non-temporal hint (one row block: as the plan says; two: the ST kernels, which the
+  // launcher picks for one-row-group plans that ask for it)
+  const PageCopy<FP8, C::NW, RBW == 1 || ST> copy(wave, lane, RBW == 1 ? (bool)args.stream : ST);
   const OperandAddr<FP8> addr(lrow, lgrp, 4 * wave);  // V^T: output column tiles 4w .. 4w+3
   unsigned char* const tiles = sm.tiles;
   using SM = KSplitSmem<FP8, RBW>;
@@ -1907,7 +1910,7 @@ static_assert(KSplitCfg<false, 1>::NW * 64 == kPartialThreads, "workgroup size")
 // Eight waves, two per SIMD; the page tiles cap residency at one workgroup per compute
 // unit, so each wave may hold up to 256 registers.
 // The leading arguments (up to the parameter block) are the ones preloaded into SGPRs.
-template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
+template <bool FP8, int RBW, bool F8QK, bool HID, bool NT, bool ST>
 __global__ __launch_bounds__(kPartialThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
     const int32_t* __restrict__ block_table, const uint8_t* __restrict__ pool, const uint16_t* __restrict__ q_ptr,
@@ -1917,21 +1920,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partial_kernel(
   __shared__ KSplitSmem<FP8, RBW> sm;
   MLA_TL(0);
   const HotArgs args(p, nwg, unit_pack, total32, len0, maxp, shape_pack, npages);
-  partial_ks<FP8, RBW, RBW == 2, F8QK, HID, NT>(p, args, q_ptr, pool, block_table, seq_lens, part_o, part_lse, sm);
+  partial_ks<FP8, RBW, RBW == 2, F8QK, HID, NT, ST>(p, args, q_ptr, pool, block_table, seq_lens, part_o, part_lse,
+                                                   sm);
 }
 
 // ------------------------------------------------------------------ launchers
 
 namespace {
 
-template <bool FP8, int RBW, bool F8QK, bool HID, bool NT>
+template <bool FP8, int RBW, bool F8QK, bool HID, bool NT, bool ST>
 void launch_partial_k(const PartialParams& p, hipStream_t stream) {
   const int32_t total32 = p.plan.n > 0 ? (int32_t)p.total_pages : 0;  // the plan path has P < 2^31
   const uint32_t unit_pack = (uint32_t)p.row_groups | (uint32_t)(p.mode & 1) << 16 | (uint32_t)p.plan.n << 17;
   const uint32_t shape_pack = (uint32_t)p.num_heads | (uint32_t)p.q_len << 16 | (uint32_t)(p.causal & 1) << 24 |
                               (uint32_t)(p.stream_pages & 1) << 25;
   const uint32_t npages = p.num_pages > (int64_t)UINT32_MAX ? UINT32_MAX : (uint32_t)p.num_pages;
-  hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, HID, NT>), dim3(partial_grid(p.num_wg, p.row_groups)),
+  hipLaunchKernelGGL((mla_partial_kernel<FP8, RBW, F8QK, HID, NT, ST>), dim3(partial_grid(p.num_wg, p.row_groups)),
                      dim3(kPartialThreads), 0, stream, p.block_table, p.pool, p.q, p.num_wg, unit_pack, total32,
                      p.plan.len[0], p.max_pages, shape_pack, npages, p, p.seq_lens, p.part_o, p.part_lse);
 }
@@ -1944,9 +1948,20 @@ hipError_t launch_partial_t(const PartialParams& p, hipStream_t stream) {
   // hidden tails get kernels of their own (the per-piece table read costs the plain
   // kernels a few percent when compiled in); non-temporal part stores as the plan says
   const bool nt = p.nt_parts && !p.hidden;
-  if (p.hidden) launch_partial_k<FP8, RBW, F8QK, true, false>(p, stream);
-  else if (nt) launch_partial_k<FP8, RBW, F8QK, false, true>(p, stream);
-  else launch_partial_k<FP8, RBW, F8QK, false, false>(p, stream);
+  // two row blocks in one row group over a large history: page copies with the
+  // non-temporal hint (spec_verify at two tokens 212 -> 189 us a layer-step; with several
+  // row groups the hint cost 3%: their pages are shared through L2)
+  if constexpr (RBW == 2) {
+    if (p.row_groups == 1 && p.stream_pages) {
+      if (p.hidden) launch_partial_k<FP8, RBW, F8QK, true, false, true>(p, stream);
+      else if (nt) launch_partial_k<FP8, RBW, F8QK, false, true, true>(p, stream);
+      else launch_partial_k<FP8, RBW, F8QK, false, false, true>(p, stream);
+      return hipGetLastError();
+    }
+  }
+  if (p.hidden) launch_partial_k<FP8, RBW, F8QK, true, false, false>(p, stream);
+  else if (nt) launch_partial_k<FP8, RBW, F8QK, false, true, false>(p, stream);
+  else launch_partial_k<FP8, RBW, F8QK, false, false, false>(p, stream);
   return hipGetLastError();
 }
 

@@ -570,6 +570,31 @@ def test_hidden_tails_reproduce_causal_and_full(B, T, H, kv, f8qk):
     assert not np.array_equal(l_c, l_n)  # the two patterns do differ
 
 
+@pytest.mark.parametrize("kv,T,H,lens,causal", [
+    ("bf16", 2, 16, [5000, 3001], True),
+    ("bf16", 2, 12, [4100, 4100], False),
+    ("fp8_e4m3fn", 1, 32, [9000, 6001], False),
+    ("fp8_e4m3fn", 2, 16, [8000, 7100], True),
+], ids=["bf16_T2_causal", "bf16_T2_H12", "fp8_H32", "fp8_T2_causal"])
+def test_streamed_two_row_blocks(kv, T, H, lens, causal):
+    """Two row blocks in one row group over more than 8 MB of KV: the kernels whose page
+    copies carry the non-temporal hint, every request and head, also with hidden tails
+    (bitwise equal to the causal plan when the tails are the causal pattern)."""
+    wl = wk.make_workload(None, seed=320 + T + H, batch=len(lens), q_len=T, num_heads=H,
+                          seq_lens=lens, kv_format=kv, shuffled=True, causal=causal)
+    assert wk.kv_bytes(wl.seq_lens, wl.kv_format) > 8 << 20
+    plan = mb.Plan(wl.batch, T, H, wl.seq_lens, wl.softmax_scale, causal=causal,
+                   kv_dtype=kv_dtype_of(wl))
+    assert plan.row_groups == 1
+    o, l = run_gpu(wl, canary=True)
+    o_ref, l_ref = run_oracle(wl)
+    compare(wl, o, l, o_ref, l_ref, "streamed two row blocks")
+    if causal:
+        tails = np.tile(np.arange(T - 1, -1, -1, dtype=np.int32), (wl.batch, 1))
+        o_h, l_h = run_gpu(dataclasses_replace(wl, causal=False), hidden=tails)
+        assert np.array_equal(o, o_h) and np.array_equal(l, l_h)
+
+
 @pytest.mark.parametrize("splits", [0, 3])
 def test_hidden_tails_one_row_block(splits):
     """One token and 12 heads (one row block): hidden tails on pieces of one page (auto
