@@ -575,7 +575,10 @@ def test_hidden_tails_reproduce_causal_and_full(B, T, H, kv, f8qk):
     ("bf16", 2, 12, [4100, 4100], False),
     ("fp8_e4m3fn", 1, 32, [9000, 6001], False),
     ("fp8_e4m3fn", 2, 16, [8000, 7100], True),
-], ids=["bf16_T2_causal", "bf16_T2_H12", "fp8_H32", "fp8_T2_causal"])
+    # KV over eight times the partial answers: ordinary part stores (the kernel that two
+    # draft tokens over a long history run)
+    ("bf16", 2, 16, [61000, 60000], True),
+], ids=["bf16_T2_causal", "bf16_T2_H12", "fp8_H32", "fp8_T2_causal", "bf16_T2_long"])
 def test_streamed_two_row_blocks(kv, T, H, lens, causal):
     """Two row blocks in one row group over more than 8 MB of KV: the kernels whose page
     copies carry the non-temporal hint, every request and head, also with hidden tails
